@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for the fused, chunked top-K KL loss.
+
+Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
+"""
+from .kd_oracle import (  # noqa: F401
+    dw_rows,
+    kd_topk_kl,
+    log_softmax_rows,
+    row_lse,
+    rows_loss_and_dh,
+    scattered_teacher,
+    teacher_distribution,
+)

@@ -1,0 +1,241 @@
+"""Plain fp64 CPU oracle for the fused, chunked top-K KL distillation loss.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+executes this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code with the
+HIP library (``top_kl_loss_amd``); both receive their inputs from the seeded
+generators in ``synth/``, which hold none of the method's arithmetic.
+
+What is computed, and where the pages say so
+--------------------------------------------
+Sources are the five web pages about the Multiverse Computing post
+"Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused
+Chunked KL Loss"; each function cites the page title and section it follows.
+
+* The teacher is run once and only its top-100 logits per token position are
+  kept ("Making Knowledge Distillation Cheap Enough to Run at Scale",
+  aipuls.nl summary, section "Summary", second paragraph).  The cache is the
+  input ``topk_idx[T,K]`` (int32) / ``topk_logit[T,K]`` (fp32).
+* The loss is a KL divergence between the teacher distribution and the
+  student's output distribution, computed over successive slices of the
+  sequence so that the dense sequence-by-vocabulary matrix never exists at
+  once (same page and section; "Hugging Face and Multiverse Computing cut KD
+  memory costs", agent-gateway.com, fourth and fifth paragraphs).
+* The direction is forward KL, teacher as the target, student
+  log-probabilities over the full vocabulary, summed over the vocabulary and
+  averaged over the selected (valid) tokens (asibiont.com article, section
+  "A Concrete Implementation Sketch").
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+
+* R1  teacher distribution = softmax over the K cached logits at temperature
+      tau (renormalised on the top-K support, no tail bucket);
+* R2  student distribution = softmax over all V logits at temperature tau;
+* R3  loss = tau^2 / N_valid * sum_t mask_t * KL_t, with N_valid = sum mask;
+      N_valid = 0 gives loss 0 and zero gradients (never NaN);
+* R4  mask: 1 = valid token, 0 = padding; ``mask=None`` means all valid;
+* R5  logits are z = H W^T with no bias and no soft-cap;
+* R6  the K ids of a row are distinct and lie in [0, V) (caller contract);
+* R7  ``chunk`` counts token rows per slice; ``chunk >= T`` is the dense form.
+
+Gradient (derived, not taken from the pages): with p = softmax(z/tau) and
+q_scat[t, v] = sum_k q[t,k] [idx[t,k] == v],
+    dL/dz[t,v] = (tau / N_valid) * mask_t * (p[t,v] - q_scat[t,v])
+because sum_k q[t,k] = 1.  Then dH = G W and dW = G^T H.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(finite differences, closed forms, library special cases, invariances);
+the pages print no worked example or loss value, so no pin comes from a
+printed number.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "teacher_distribution",
+    "log_softmax_rows",
+    "kd_topk_kl",
+    "row_lse",
+    "rows_loss_and_dh",
+    "dw_rows",
+    "scattered_teacher",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def log_softmax_rows(s):
+    """Row-wise log-softmax of a 2-D fp64 array (max-shifted logsumexp).
+
+    Student side of R2: the full-vocabulary log-probabilities (asibiont.com,
+    "A Concrete Implementation Sketch": the student log-softmax over the
+    vocabulary).  Returns (log_p, lse).
+    """
+    s = _f64(s)
+    m = s.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    return s - lse[:, None], lse
+
+
+def teacher_distribution(topk_logit, tau):
+    """Teacher probabilities over the cached top-K support (reading R1).
+
+    The cache holds the teacher's top-K logits per position (aipuls.nl,
+    "Summary"); they are divided by tau and renormalised over the K slots.
+    Returns (q, log_q), each [T, K] fp64.
+    """
+    u = _f64(topk_logit) / float(tau)
+    log_q, _ = log_softmax_rows(u)
+    return np.exp(log_q), log_q
+
+
+def scattered_teacher(topk_idx, q, V):
+    """Dense [rows, V] fp64 array with q[t,k] added at column topk_idx[t,k]."""
+    rows, K = topk_idx.shape
+    out = np.zeros((rows, V), dtype=np.float64)
+    r = np.repeat(np.arange(rows), K)
+    np.add.at(out, (r, np.asarray(topk_idx).reshape(-1)), q.reshape(-1))
+    return out
+
+
+def _mask_vector(mask, T):
+    if mask is None:
+        return np.ones(T, dtype=np.float64)
+    return (np.asarray(mask).reshape(T) != 0).astype(np.float64)
+
+
+def kd_topk_kl(H, W, topk_idx, topk_logit, mask, tau, chunk=None):
+    """Loss and analytic gradients of the chunked top-K KL (readings R1-R7).
+
+    Follows the pages' description of the fused, chunked loss: the token
+    rows are processed in successive slices of ``chunk`` rows; for each slice
+    the dense logits z = H_c W^T are formed (the sequence-by-vocabulary tensor
+    of "Hugging Face and Multiverse Computing cut KD memory costs",
+    agent-gateway.com, fourth paragraph, restricted to one slice), the
+    student log-softmax is taken over the whole vocabulary, and the forward
+    KL against the teacher's top-K distribution is accumulated together with
+    its gradient before the slice is discarded (aipuls.nl, "Summary").
+
+    Inputs are upcast exactly to fp64 (bf16 inputs arrive as their exact
+    fp32 values).  Returns a dict with fp64 ``loss`` (scalar), ``row_loss``
+    [T] (mask_t * KL_t, before the tau^2/N scaling), ``dH`` [T,d], ``dW``
+    [V,d], ``lse`` [T] (logsumexp of z/tau) and ``n_valid``.
+    """
+    H = _f64(H)
+    W = _f64(W)
+    topk_idx = np.asarray(topk_idx, dtype=np.int64)
+    T, d = H.shape
+    V = W.shape[0]
+    K = topk_idx.shape[1]
+    assert W.shape[1] == d and topk_idx.shape == (T, K)
+    assert topk_logit.shape == (T, K)
+    tau = float(tau)
+    m = _mask_vector(mask, T)
+    n_valid = float(m.sum())
+    # R3: loss scale tau^2/N and gradient scale tau/N; N = 0 gives zeros.
+    loss_scale = tau * tau / n_valid if n_valid > 0 else 0.0
+    grad_scale = tau / n_valid if n_valid > 0 else 0.0
+
+    q, log_q = teacher_distribution(topk_logit, tau)
+    chunk = T if chunk is None else max(1, min(int(chunk), T))
+
+    row_loss = np.zeros(T)
+    lse_all = np.zeros(T)
+    dH = np.zeros((T, d))
+    dW = np.zeros((V, d))
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        rows = np.arange(c0, c1)
+        z = H[c0:c1] @ W.T                               # dense slice [C, V]
+        log_p, lse = log_softmax_rows(z / tau)           # R2
+        lse_all[c0:c1] = lse
+        ids = topk_idx[c0:c1]
+        log_p_at = log_p[np.arange(c1 - c0)[:, None], ids]   # [C, K]
+        # forward KL(q || p) on the teacher's support, one value per row
+        kl = (q[c0:c1] * (log_q[c0:c1] - log_p_at)).sum(axis=1)
+        row_loss[c0:c1] = m[rows] * kl
+        # dL/dz = tau/N * mask * (p - q_scat)
+        G = np.exp(log_p) - scattered_teacher(ids, q[c0:c1], V)
+        G *= (grad_scale * m[rows])[:, None]
+        dH[c0:c1] = G @ W
+        dW += G.T @ H[c0:c1]
+    loss = loss_scale * row_loss.sum()
+    return {
+        "loss": loss,
+        "row_loss": row_loss,
+        "dH": dH,
+        "dW": dW,
+        "lse": lse_all,
+        "n_valid": n_valid,
+    }
+
+
+def row_lse(H_rows, W, tau, rows_per_block=256):
+    """logsumexp_v(z[t,v]/tau) for the given rows only (reading R2).
+
+    The same student normaliser as ``kd_topk_kl``, evaluated row block by
+    row block so that full-size inputs fit in host memory.
+    """
+    H_rows = _f64(H_rows)
+    W = _f64(W)
+    out = np.empty(H_rows.shape[0])
+    for r0 in range(0, H_rows.shape[0], rows_per_block):
+        z = H_rows[r0:r0 + rows_per_block] @ W.T
+        _, lse = log_softmax_rows(z / float(tau))
+        out[r0:r0 + rows_per_block] = lse
+    return out
+
+
+def rows_loss_and_dh(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
+    """Per-row KL and dH rows for a sample of token rows.
+
+    A row's KL and its dH row depend only on that row and on N_valid (a
+    count of the mask), so sampled rows of a full-size problem can be
+    checked one by one.  Returns (row_loss [R] = mask*KL, dH [R,d]).
+    """
+    H_rows = _f64(H_rows)
+    W = _f64(W)
+    tau = float(tau)
+    R = H_rows.shape[0]
+    m = _mask_vector(mask_rows, R)
+    grad_scale = tau / n_valid if n_valid > 0 else 0.0
+    q, log_q = teacher_distribution(logit_rows, tau)
+    z = H_rows @ W.T
+    log_p, _ = log_softmax_rows(z / tau)
+    ids = np.asarray(idx_rows, dtype=np.int64)
+    log_p_at = log_p[np.arange(R)[:, None], ids]
+    kl = (q * (log_q - log_p_at)).sum(axis=1)
+    G = np.exp(log_p) - scattered_teacher(ids, q, W.shape[0])
+    G *= (grad_scale * m)[:, None]
+    return m * kl, G @ W
+
+
+def dw_rows(H, W, topk_idx, topk_logit, mask, tau, lse, v_rows):
+    """Selected rows of dW = G^T H, given every token's student lse.
+
+    dW[v] = sum_t G[t,v] H[t] needs column v of G for all T tokens, which
+    needs lse_t of every row (from ``row_lse``) but only the logits z[:, v]
+    of the selected vocabulary rows.  Returns dW[v_rows] [len(v_rows), d].
+    """
+    H = _f64(H)
+    tau = float(tau)
+    T = H.shape[0]
+    v_rows = np.asarray(v_rows, dtype=np.int64)
+    m = _mask_vector(mask, T)
+    n_valid = m.sum()
+    grad_scale = tau / n_valid if n_valid > 0 else 0.0
+    q, _ = teacher_distribution(topk_logit, tau)
+    Wv = _f64(W)[v_rows]                         # [R, d]
+    z = H @ Wv.T                                 # [T, R]
+    p = np.exp(z / tau - _f64(lse)[:, None])
+    ids = np.asarray(topk_idx, dtype=np.int64)
+    qs = np.zeros_like(p)
+    for j, v in enumerate(v_rows):
+        hit = ids == v                           # [T, K]
+        qs[:, j] = (q * hit).sum(axis=1)
+    G = (p - qs) * (grad_scale * m)[:, None]     # [T, R]
+    return G.T @ H
