@@ -1,0 +1,143 @@
+/*
+ * kd_topk_kl.h -- C ABI of the fused, chunked top-K KL distillation loss
+ * (forward + backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed
+ * ----------------
+ * The method is the one described in "Efficient Knowledge Distillation for
+ * LLMs: Offline Top-K Logits and a Fused Chunked KL Loss" as reported by
+ * "Making Knowledge Distillation Cheap Enough to Run at Scale" (aipuls.nl,
+ * section "Summary") and "Hugging Face and Multiverse Computing cut KD
+ * memory costs" (agent-gateway.com): the teacher's top-K logits per token
+ * are cached offline, and the KL loss between the teacher's distribution and
+ * the student's LM-head output is evaluated over successive token slices,
+ * so that the sequence-by-vocabulary logit matrix never exists in memory.
+ *
+ * For token t (0 <= t < T), with z[t,v] = sum_j H[t,j] W[v,j] (no bias):
+ *   p[t,:]  = softmax over all V of z[t,:]/tau          (student)
+ *   q[t,k]  = softmax over the K slots of topk_logit[t,:]/tau  (teacher)
+ *   KL_t    = sum_k q[t,k] (log q[t,k] - log p[t, topk_idx[t,k]])
+ *   N       = sum_t mask[t]   (mask NULL: N = T)
+ *   loss    = tau^2 / N * sum_t mask[t] KL_t            (0 when N = 0)
+ *   G[t,v]  = tau / N * mask[t] * (p[t,v] - sum_k q[t,k] [topk_idx[t,k]==v])
+ *   dH      = G W        dW = G^T H      (dW optionally accumulated)
+ * The direction (teacher as target, student log-softmax over the whole
+ * vocabulary, mean over selected tokens) follows the asibiont.com article,
+ * section "A Concrete Implementation Sketch"; temperature scaling by tau and
+ * tau^2 is this library's reading where the pages are silent.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensors are dense, row-major, contiguous, in device memory of the
+ *   current HIP device; the caller allocates and owns every buffer.  The
+ *   library allocates nothing and keeps no state between calls.
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *   the default stream).  Outputs are valid once that stream has
+ *   synchronised.  No call synchronises the host.
+ * - Return value: KD_OK or one KD_ERR_* code.  Every argument check runs on
+ *   the host before any HIP call, so a rejected call enqueues nothing.
+ *   KD_ERR_HIP reports a failed launch; kd_status_string() then includes
+ *   the HIP error text of the last failure on the calling thread.
+ * - Calls on different streams may run concurrently when each has its own
+ *   workspace and outputs.
+ */
+#ifndef KD_TOPK_KL_H
+#define KD_TOPK_KL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of H and W. */
+typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+enum {
+  KD_OK = 0,
+  KD_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, K > V, bad tau */
+  KD_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required    */
+  KD_ERR_UNSUPPORTED = 3, /* valid but unsupported: d % 8 != 0, K > KD_MAX_K,
+                             sizes beyond 32-bit index range, unknown dtype */
+  KD_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
+};
+
+/* Flags for kd_topk_kl_fwd_bwd. */
+enum {
+  KD_FLAG_ACCUMULATE_DW = 1u /* dW += G^T H instead of dW = G^T H          */
+};
+
+/* Largest supported K (teacher cache width). */
+#define KD_MAX_K 1024
+
+/*
+ * kd_topk_kl_workspace_size -- bytes of scratch device memory needed by
+ * kd_topk_kl_fwd_bwd for these sizes.
+ *
+ * The workspace holds the per-slice intermediates of the chunked loss
+ * ("Making Knowledge Distillation Cheap Enough to Run at Scale", aipuls.nl,
+ * section "Summary": memory bounded by one slice): the slice's shifted
+ * student probabilities (chunk x V, in the input element type), per-row
+ * and per-vocabulary-segment softmax statistics, the teacher distribution
+ * of the slice, split-K partial sums of dH for the slice, and O(T) per-row
+ * scalars.  It grows with chunk*V and chunk*d, never with T*V.
+ *
+ * Arguments: sizes as for kd_topk_kl_fwd_bwd; `chunk` is clamped to [1, T].
+ * `bytes_out` (host pointer) receives the size.  Returns KD_OK,
+ * KD_ERR_INVALID_ARG (bad sizes or NULL bytes_out) or KD_ERR_UNSUPPORTED.
+ */
+int kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                              int32_t chunk, kd_dtype dtype,
+                              size_t *bytes_out);
+
+/*
+ * kd_topk_kl_fwd_bwd -- loss, dH and dW of the top-K KL distillation loss,
+ * processed in token slices of `chunk` rows (the fused, chunked loss of
+ * "Hugging Face and Multiverse Computing cut KD memory costs",
+ * agent-gateway.com; the offline top-K cache of "Making Knowledge
+ * Distillation Cheap Enough to Run at Scale", aipuls.nl, section "Summary").
+ *
+ *   H          [T, d]  student final hidden states, dtype (bf16 or fp32)
+ *   W          [V, d]  student LM-head weight, dtype
+ *   dtype      element type of H and W
+ *   topk_idx   [T, K]  int32 teacher top-K vocabulary ids.  Contract: each
+ *                      row holds K distinct ids in [0, V).  Ids outside
+ *                      [0, V) are never dereferenced (memory-safe) but the
+ *                      results for their rows are unspecified.
+ *   topk_logit [T, K]  fp32 teacher logits of those ids (any order)
+ *   mask       [T]     uint8, 1 = valid token, 0 = padding; NULL = all valid
+ *   T, d, V, K         sizes; T, d, V, K >= 1, K <= V, K <= KD_MAX_K,
+ *                      d % 8 == 0, T*d, V*d, T*K < 2^31
+ *   tau        temperature, finite and > 0
+ *   chunk      token rows per slice (>= 1; clamped to T)
+ *   flags      0 or KD_FLAG_ACCUMULATE_DW
+ *   loss       [1]     fp32 output (device)
+ *   row_loss   [T]     fp32 output mask[t]*KL_t (unscaled), or NULL
+ *   dH         [T, d]  fp32 output (overwritten)
+ *   dW         [V, d]  fp32 output (overwritten, or accumulated into)
+ *   workspace  device scratch of at least kd_topk_kl_workspace_size()
+ *              bytes, 256-byte aligned; its contents on entry are ignored
+ *   stream     hipStream_t (as void*) on which all work is enqueued
+ *
+ * Defined edge results: N = 0 gives loss = 0, dH = 0 and a zero dW
+ * contribution; a padding row t gives dH[t,:] = 0 and row_loss[t] = 0.
+ * Reductions are ordered, so repeated calls give bitwise-identical results.
+ */
+int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
+                       const int32_t *topk_idx, const float *topk_logit,
+                       const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                       int32_t K, float tau, int32_t chunk, uint32_t flags,
+                       float *loss, float *row_loss, float *dH, float *dW,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code.  For KD_ERR_HIP the
+ * text also carries the HIP error string of the last failure on the calling
+ * thread.  Never NULL. */
+const char *kd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_TOPK_KL_H */

@@ -1,0 +1,112 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, sizes its workspace, and rejects bad arguments before any
+HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_kl_loss_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_topk_kl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kd.LIB_PATH),
+                                reason="libkdtopk.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kd_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    assert declared_functions() == sorted(kd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(5):
+        assert kd.kd_status_string(s).startswith(
+            ["KD_OK", "KD_ERR_INVALID_ARG", "KD_ERR_WORKSPACE",
+             "KD_ERR_UNSUPPORTED", "KD_ERR_HIP"][s])
+    assert kd.kd_status_string(99) == "unknown kd status"
+
+
+def test_workspace_size_scales_with_chunk_not_with_T():
+    a = kd.kd_topk_kl_workspace_size(32768, 2880, 201088, 100, 1024, kd.KD_BF16)
+    b = kd.kd_topk_kl_workspace_size(4096, 2880, 201088, 100, 1024, kd.KD_BF16)
+    dense = 8 * 32768 * 201088          # fp32 logits + fp32 gradient
+    assert a < dense / 50
+    assert a - b < 32768 * 4 * 2        # only O(T) scalars grow with T
+    c = kd.kd_topk_kl_workspace_size(32768, 2880, 201088, 100, 2048, kd.KD_BF16)
+    assert 1.8 * a < c < 2.2 * a
+    # chunk is clamped to T
+    assert (kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 64, kd.KD_F32) <
+            kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 10 ** 6, kd.KD_F32)
+            == kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 256, kd.KD_F32))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 512, 8192, 100, 64, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 0, 8192, 100, 64, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 0, 100, 64, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 8192, 0, 64, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 99, 100, 64, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 8192, 100, 0, kd.KD_F32), kd.KD_ERR_INVALID_ARG),
+    ((256, 510, 8192, 100, 64, kd.KD_F32), kd.KD_ERR_UNSUPPORTED),
+    ((256, 512, 8192, 2000, 64, kd.KD_F32), kd.KD_ERR_UNSUPPORTED),
+    ((256, 512, 8192, 100, 64, 7), kd.KD_ERR_UNSUPPORTED),
+    ((2 ** 20, 4096, 8192, 100, 64, kd.KD_F32), kd.KD_ERR_UNSUPPORTED),
+])
+def test_workspace_size_rejects(args, code):
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_topk_kl_workspace_size(*args)
+    assert e.value.status == code
+
+
+def _call(**kw):
+    lib = kd.load_library()
+    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, loss=1,
+             row_loss=None, dH=1, dW=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kd_topk_kl_fwd_bwd(
+        a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
+        a["d"], a["V"], a["K"], a["tau"], a["chunk"], a["flags"], a["loss"],
+        a["row_loss"], a["dH"], a["dW"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=None), kd.KD_ERR_INVALID_ARG),
+    (dict(W=None), kd.KD_ERR_INVALID_ARG),
+    (dict(idx=None), kd.KD_ERR_INVALID_ARG),
+    (dict(logit=None), kd.KD_ERR_INVALID_ARG),
+    (dict(loss=None), kd.KD_ERR_INVALID_ARG),
+    (dict(dH=None), kd.KD_ERR_INVALID_ARG),
+    (dict(dW=None), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=0.0), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=-1.0), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=float("inf")), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), kd.KD_ERR_INVALID_ARG),
+    (dict(flags=4), kd.KD_ERR_INVALID_ARG),
+    (dict(chunk=0), kd.KD_ERR_INVALID_ARG),
+    (dict(K=9000), kd.KD_ERR_INVALID_ARG),
+    (dict(T=-5), kd.KD_ERR_INVALID_ARG),
+    (dict(d=12), kd.KD_ERR_UNSUPPORTED),
+    (dict(dtype=3), kd.KD_ERR_UNSUPPORTED),
+    (dict(K=1025), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=None), kd.KD_ERR_WORKSPACE),
+    (dict(ws_bytes=100), kd.KD_ERR_WORKSPACE),
+    (dict(ws=256 + 16), kd.KD_ERR_WORKSPACE),
+])
+def test_fwd_bwd_rejects_before_any_hip_call(kw, code):
+    assert _call(**kw) == code

@@ -1,0 +1,147 @@
+"""Python binding of libkdtopk.so, the MI355X fused chunked top-K KL loss.
+
+Argument marshalling only: every step of the loss runs in the HIP kernels of
+the C library (``include/kd_topk_kl.h``).  PyTorch provides device memory
+and the current stream.  There is no fallback: if the library is missing or
+cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "KD_F32", "KD_BF16", "KD_FLAG_ACCUMULATE_DW", "KD_MAX_K", "LIB_PATH",
+    "KdError", "load_library", "kd_topk_kl_workspace_size",
+    "kd_topk_kl_fwd_bwd", "kd_status_string", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
+
+KD_F32, KD_BF16 = 0, 1
+KD_OK, KD_ERR_INVALID_ARG, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP = range(5)
+KD_FLAG_ACCUMULATE_DW = 1
+KD_MAX_K = 1024
+EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
+                    "kd_status_string")
+
+_lib = None
+
+
+class KdError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkdtopk.so and declare its C signatures (once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m top_kl_loss_amd.build` "
+            "(needs ROCm hipcc)")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    lib.kd_topk_kl_workspace_size.argtypes = [
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_int,
+        c.POINTER(c.c_size_t)]
+    lib.kd_topk_kl_workspace_size.restype = c.c_int
+    lib.kd_topk_kl_fwd_bwd.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
+        c.c_uint32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_void_p, c.c_size_t, c.c_void_p]
+    lib.kd_topk_kl_fwd_bwd.restype = c.c_int
+    lib.kd_status_string.argtypes = [c.c_int]
+    lib.kd_status_string.restype = c.c_char_p
+    _lib = lib
+    return lib
+
+
+def kd_status_string(status: int) -> str:
+    return load_library().kd_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != KD_OK:
+        raise KdError(status, kd_status_string(status))
+
+
+def kd_topk_kl_workspace_size(T, d, V, K, chunk, dtype) -> int:
+    """Workspace bytes for kd_topk_kl_fwd_bwd (see the C header)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_topk_kl_workspace_size(
+        int(T), int(d), int(V), int(K), int(chunk), int(dtype),
+        ctypes.byref(out)))
+    return out.value
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KD_BF16
+    if t.dtype == torch.float32:
+        return KD_F32
+    raise TypeError(f"H/W must be bfloat16 or float32, got {t.dtype}")
+
+
+def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                       chunk=None, flags=0, *, dW=None, row_loss=True,
+                       workspace=None, stream=None):
+    """Loss, per-row KL, dH and dW of the top-K KL loss on the GPU.
+
+    H [T,d] and W [V,d] (bf16 or fp32), topk_idx [T,K] int32, topk_logit
+    [T,K] fp32 and mask [T] (uint8/bool or None) are CUDA tensors.  Outputs
+    are allocated here (``dW`` may be passed in, e.g. with
+    KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW),
+    enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    lib = load_library()
+    T, d = H.shape
+    V = W.shape[0]
+    K = topk_idx.shape[1]
+    chunk = T if chunk is None else int(chunk)
+    dt = _dtype_code(H)
+    if W.dtype != H.dtype or W.shape[1] != d:
+        raise ValueError("W must be [V, d] with H's dtype")
+    if topk_idx.dtype != torch.int32 or tuple(topk_idx.shape) != (T, K):
+        raise ValueError("topk_idx must be int32 [T, K]")
+    if topk_logit.dtype != torch.float32 or tuple(topk_logit.shape) != (T, K):
+        raise ValueError("topk_logit must be float32 [T, K]")
+    tensors = [H, W, topk_idx, topk_logit]
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.numel() != T:
+            raise ValueError("mask must be uint8/bool [T]")
+        tensors.append(mask)
+    dev = H.device
+    for t in tensors:
+        if not t.is_cuda or t.device != dev or not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous tensors on one GPU")
+    ws_bytes = kd_topk_kl_workspace_size(T, d, V, K, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    rl = torch.empty(T, **f32) if row_loss else None
+    dH = torch.empty(T, d, **f32)
+    if dW is None:
+        dW = torch.empty(V, d, **f32)
+    elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
+        raise ValueError("dW must be float32 [V, d]")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.kd_topk_kl_fwd_bwd(
+        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
+        T, d, V, K, float(tau), chunk, int(flags), loss.data_ptr(),
+        rl.data_ptr() if rl is not None else None, dH.data_ptr(),
+        dW.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
+    return loss, rl, dH, dW

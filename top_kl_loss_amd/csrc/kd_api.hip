@@ -1,0 +1,177 @@
+// C ABI of the fused, chunked top-K KL loss: argument checks, workspace
+// layout and the slice loop that enqueues the kernels on the caller's
+// stream.  The loop follows the pages' description of the loss ("Making
+// Knowledge Distillation Cheap Enough to Run at Scale", aipuls.nl, section
+// "Summary": successive slices are processed and discarded, so memory is
+// bounded by one slice).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kd_internal.h"
+#include "kd_topk_kl.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+struct Layout {
+  int C, nseg, ldp, splits;
+  size_t esize;
+  size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
+      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp;
+  size_t total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
+                kd_dtype dtype) {
+  if (T < 1 || d < 1 || V < 1 || K < 1 || chunk < 1 || K > V)
+    return KD_ERR_INVALID_ARG;
+  if (dtype != KD_F32 && dtype != KD_BF16) return KD_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || K > KD_MAX_K) return KD_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  if (T * d >= lim || V * d >= lim || T * K >= lim || V >= lim - kd::SEG)
+    return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
+                   kd_dtype dtype) {
+  Layout L{};
+  L.C = (int)(chunk < T ? chunk : T);
+  L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
+  L.ldp = L.nseg * kd::SEG;
+  L.splits = kd::dh_splits(L.C, (int)d, L.nseg);
+  L.esize = dtype == KD_BF16 ? 2 : 4;
+  const size_t C = L.C, nseg = L.nseg;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  L.o_scal = take(sizeof(kd::Scalars));
+  L.o_rowloss = take(sizeof(float) * (size_t)T);
+  L.o_q = take(sizeof(float) * C * K);
+  L.o_cterm = take(sizeof(float) * C);
+  L.o_zg = take(sizeof(float) * C * K);
+  L.o_sid = take(sizeof(int32_t) * C * K);
+  L.o_sslot = take(sizeof(int32_t) * C * K);
+  L.o_first = take(sizeof(int16_t) * C * nseg);
+  L.o_mseg = take(sizeof(float) * C * nseg);
+  L.o_sseg = take(sizeof(float) * C * nseg);
+  L.o_fseg = take(sizeof(float) * C * nseg);
+  L.o_lse = take(sizeof(float) * C);
+  L.o_P = take(L.esize * C * (size_t)L.ldp);
+  L.o_dhp = take(sizeof(float) * (size_t)L.splits * C * (size_t)d);
+  L.total = o;
+  return L;
+}
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error: %s", hipGetErrorString(e));
+  return KD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                              int32_t chunk, kd_dtype dtype, size_t *bytes_out) {
+  if (!bytes_out) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  *bytes_out = make_layout(T, d, V, K, chunk, dtype).total;
+  return KD_OK;
+}
+
+int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
+                       const int32_t *topk_idx, const float *topk_logit,
+                       const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                       int32_t K, float tau, int32_t chunk, uint32_t flags,
+                       float *loss, float *row_loss, float *dH, float *dW,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW)
+    return KD_ERR_INVALID_ARG;
+  if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
+  if (flags & ~uint32_t(KD_FLAG_ACCUMULATE_DW)) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  const Layout L = make_layout(T, d, V, K, chunk, dtype);
+  if (!workspace || workspace_bytes < L.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return KD_ERR_WORKSPACE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const bool bf16 = dtype == KD_BF16;
+  kd::Scalars *scal = reinterpret_cast<kd::Scalars *>(ws + L.o_scal);
+  float *rl = row_loss ? row_loss : reinterpret_cast<float *>(ws + L.o_rowloss);
+
+  kd::SliceArgs a{};
+  a.H = H;
+  a.W = W;
+  a.topk_idx = topk_idx;
+  a.topk_logit = topk_logit;
+  a.mask = mask;
+  a.scal = scal;
+  a.T = (int)T;
+  a.d = (int)d;
+  a.V = (int)V;
+  a.K = K;
+  a.nseg = L.nseg;
+  a.ldp = L.ldp;
+  a.inv_tau = 1.0f / tau;
+  a.q = reinterpret_cast<float *>(ws + L.o_q);
+  a.cterm = reinterpret_cast<float *>(ws + L.o_cterm);
+  a.zg = reinterpret_cast<float *>(ws + L.o_zg);
+  a.sid = reinterpret_cast<int32_t *>(ws + L.o_sid);
+  a.sslot = reinterpret_cast<int32_t *>(ws + L.o_sslot);
+  a.first = reinterpret_cast<int16_t *>(ws + L.o_first);
+  a.mseg = reinterpret_cast<float *>(ws + L.o_mseg);
+  a.sseg = reinterpret_cast<float *>(ws + L.o_sseg);
+  a.fseg = reinterpret_cast<float *>(ws + L.o_fseg);
+  a.lse = reinterpret_cast<float *>(ws + L.o_lse);
+  a.P = ws + L.o_P;
+  a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
+  a.dh_stride = (size_t)L.C * (size_t)d;
+  a.splits = L.splits;
+  a.row_loss = rl;
+  a.dH = dH;
+  a.dW = dW;
+
+  hipError_t e = kd::launch_valid_count(mask, (int)T, tau, scal, s);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int64_t c0 = 0; c0 < T; c0 += L.C) {
+    a.c0 = c0;
+    a.C = (int)(T - c0 < L.C ? T - c0 : L.C);
+    a.dw_beta = (c0 > 0 || (flags & KD_FLAG_ACCUMULATE_DW)) ? 1 : 0;
+    if ((e = kd::launch_prep_rows(a, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kd::launch_gemm_logits(a, bf16, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kd::launch_lse_fix(a, bf16, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kd::launch_gemm_dh(a, bf16, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kd::launch_reduce_dh(a, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kd::launch_gemm_dw(a, bf16, s)) != hipSuccess) return hip_fail(e);
+  }
+  if ((e = kd::launch_final_loss(rl, (int)T, scal, loss, s)) != hipSuccess)
+    return hip_fail(e);
+  return KD_OK;
+}
+
+const char *kd_status_string(int status) {
+  switch (status) {
+    case KD_OK: return "KD_OK: success";
+    case KD_ERR_INVALID_ARG:
+      return "KD_ERR_INVALID_ARG: null pointer, non-positive size, K > V, "
+             "chunk < 1, unknown flag or tau not finite and positive";
+    case KD_ERR_WORKSPACE:
+      return "KD_ERR_WORKSPACE: workspace missing, smaller than "
+             "kd_topk_kl_workspace_size() or not 256-byte aligned";
+    case KD_ERR_UNSUPPORTED:
+      return "KD_ERR_UNSUPPORTED: d % 8 != 0, K > KD_MAX_K, unknown dtype or "
+             "sizes beyond the 32-bit index range";
+    case KD_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "KD_ERR_HIP: HIP error";
+    default: return "unknown kd status";
+  }
+}
+
+}  // extern "C"

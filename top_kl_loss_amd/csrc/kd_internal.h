@@ -1,0 +1,85 @@
+// Internal declarations shared by the launcher and the kernel translation
+// units of the fused, chunked top-K KL loss.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kd {
+
+// Width of one vocabulary segment.  The logits GEMM uses it as its N tile,
+// so the per-row softmax statistics come in segments of this many
+// vocabulary entries; the backward GEMMs align their tiles to it.
+constexpr int SEG = 256;
+
+// A segment's stored probabilities are shifted by the segment's own maximum.
+// When the row's logsumexp lies more than this far (in units of z/tau)
+// above a segment maximum that carries teacher ids, the segment is shifted
+// again so that the teacher correction stays finite in the stored type.
+constexpr float RESHIFT_NATS = 60.0f;
+
+// Device-resident scalars written once per call.
+struct Scalars {
+  int32_t n_valid;
+  float grad_scale;  // tau / N  (0 when N == 0)
+  float loss_scale;  // tau^2 / N (0 when N == 0)
+  int32_t pad[61];
+};
+
+// Everything one slice of `C` token rows needs.  Pointers are device
+// pointers.  Row r of the slice is token c0 + r.
+struct SliceArgs {
+  const void *H;            // [T, d] element type
+  const void *W;            // [V, d] element type
+  const int32_t *topk_idx;  // [T, K]
+  const float *topk_logit;  // [T, K]
+  const uint8_t *mask;      // [T] or nullptr
+  const Scalars *scal;
+  int64_t c0;
+  int C;       // rows in this slice
+  int T, d, V, K;
+  int nseg;    // ceil(V / SEG)
+  int ldp;     // nseg * SEG, row pitch of P in elements
+  float inv_tau;
+  // workspace views (slice-local, row r)
+  float *q;          // [Cmax, K] teacher probabilities
+  float *cterm;      // [Cmax] sum_k q log q
+  float *zg;         // [Cmax, K] student logit at each teacher slot
+  int32_t *sid;      // [Cmax, K] teacher ids sorted ascending
+  int32_t *sslot;    // [Cmax, K] slot of each sorted id
+  int16_t *first;    // [Cmax, nseg] first sorted position in segment or -1
+  float *mseg;       // [Cmax, nseg] segment max of z/tau (shift)
+  float *sseg;       // [Cmax, nseg] segment sum of exp(z/tau - shift)
+  float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
+  float *lse;        // [Cmax] row logsumexp of z/tau
+  void *P;           // [Cmax, ldp] shifted probabilities (element type)
+  float *dh_part;    // [splits, Cmax, d] split-K partial sums of dH
+  size_t dh_stride;  // elements between two partials (Cmax * d)
+  int splits;
+  float *row_loss;   // [T] mask * KL_t
+  float *dH;         // [T, d]
+  float *dW;         // [V, d]
+  int dw_beta;       // 0: dW = G^T H, 1: dW += G^T H
+};
+
+// Tile shapes of the three GEMMs (all use 256-thread workgroups).
+constexpr int G1_BM = 128, G1_BN = SEG;   // logits:  C x V, K = d
+constexpr int DH_BM = 128, DH_BN = 128;   // dH:      C x d, K = V (split)
+constexpr int DW_BM = 128, DW_BN = 128;   // dW:      V x d, K = C
+
+int dh_splits(int C, int d, int nseg);
+
+// Launch wrappers; each returns hipSuccess or the launch error.
+hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,
+                              Scalars *scal, hipStream_t s);
+hipError_t launch_prep_rows(const SliceArgs &a, hipStream_t s);
+hipError_t launch_lse_fix(const SliceArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_reduce_dh(const SliceArgs &a, hipStream_t s);
+hipError_t launch_final_loss(const float *row_loss, int T,
+                             const Scalars *scal, float *loss, hipStream_t s);
+hipError_t launch_gemm_logits(const SliceArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_gemm_dh(const SliceArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_gemm_dw(const SliceArgs &a, bool bf16, hipStream_t s);
+
+}  // namespace kd
