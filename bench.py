@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused, chunked top-K KL loss (forward + backward) on one
+MI355X.
+
+One step = one kd_topk_kl_fwd_bwd call over the whole synthetic batch
+(every slice: teacher softmax, logits GEMM with softmax statistics and
+gather, teacher correction, dH and dW GEMMs, loss), inputs resident in HBM.
+Prints one JSON line:
+  value      tokens/s over the whole job (T * steps / wall time)
+  roofline   the dominant kernel's achieved TFLOP/s (algorithmic flops per
+             launch / mean launch time from HIP events recorded around its
+             launches on the library's stream during the timed steps)
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s & TFLOP/s fused top-K KL fwd+bwd, T=32k V=201k; % bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+GEMM_KERNELS = {2: "gemm_logits", 4: "gemm_dh", 6: "gemm_dw"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_kl_loss_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, launches_per_step):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(x, target_s):
+    """The oracle, as it stands, on the first R tokens of the workload."""
+    import numpy as np
+    from oracle import kd_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) \
+            if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+
+    def run(R):
+        m = None if x.mask is None else x.mask[:R]
+        t0 = time.perf_counter()
+        orc.kd_topk_kl(x.H[:R], x.W, x.topk_idx[:R], x.topk_logit[:R], m,
+                       x.tau, chunk=R)
+        return time.perf_counter() - t0
+
+    R = 8
+    dt = run(R)
+    per = dt / R
+    R = int(max(8, min(x.T, 2048, target_s / max(per, 1e-9))))
+    log(f"cpu baseline: oracle on {R} tokens (~{per * R:.0f} s)")
+    dt = run(R)
+    return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {R} of {x.T} tokens of {x.name} "
+                      f"(full d={x.d}, V={x.V}, K={x.K}), fp64 NumPy, one "
+                      f"chunk; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t32k")
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU "
+              f"path (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+
+    torch.cuda.init()
+    lib = kd.load_library()
+    log(f"generating workload {args.workload}")
+    t0 = time.perf_counter()
+    x = synth.workload(args.workload, teacher_device="cuda")
+    chunk = args.chunk or x.chunk
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s: T={x.T} d={x.d} "
+        f"V={x.V} K={x.K} {x.dtype} tau={x.tau} chunk={chunk}")
+    dev = torch.device("cuda:0")
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        dt_code = kd.KD_BF16
+    else:
+        H = torch.from_numpy(x.H).to(dev)
+        W = torch.from_numpy(x.W).to(dev)
+        dt_code = kd.KD_F32
+    idx = torch.from_numpy(x.topk_idx).to(dev)
+    lg = torch.from_numpy(x.topk_logit).to(dev)
+    mask = None if x.mask is None else torch.from_numpy(x.mask).to(dev)
+    T, d, V, K = x.T, x.d, x.V, x.K
+    ws_bytes = kd.kd_topk_kl_workspace_size(T, d, V, K, chunk, dt_code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    rl = torch.empty(T, **f32)
+    dH = torch.empty(T, d, **f32)
+    dW = torch.empty(V, d, **f32)
+    torch.cuda.synchronize()
+    hip.set_device(0)
+    stream = hip.Stream()
+
+    def step():
+        st = lib.kd_topk_kl_fwd_bwd(
+            H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+            None if mask is None else mask.data_ptr(), T, d, V, K,
+            float(x.tau), chunk, 0, loss.data_ptr(), rl.data_ptr(),
+            dH.data_ptr(), dW.data_ptr(), ws.data_ptr(), ws_bytes, stream.value)
+        if st != 0:
+            raise RuntimeError(kd.kd_status_string(st))
+
+    n_chunks = (T + chunk - 1) // chunk
+    launches_per_step = 2 + 6 * n_chunks
+
+    def run_logged(mask_bits, n_steps, cap):
+        """Run n_steps with the launch log on; returns [(kind, ms)]."""
+        starts = [hip.Event() for _ in range(cap)]
+        ends = [hip.Event() for _ in range(cap)]
+        arr_s = (ctypes.c_void_p * cap)(*[e.value for e in starts])
+        arr_e = (ctypes.c_void_p * cap)(*[e.value for e in ends])
+        kinds = (ctypes.c_int32 * cap)()
+        count = ctypes.c_int32(0)
+        kd.kd_set_launch_log(mask_bits, arr_s, arr_e, kinds, cap,
+                             ctypes.byref(count))
+        try:
+            for _ in range(n_steps):
+                step()
+            stream.synchronize()
+        finally:
+            kd.kd_set_launch_log(0, None, None, None, 0, None)
+        return [(kinds[i], starts[i].elapsed_ms(ends[i]))
+                for i in range(count.value)]
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+
+    # One logged step over every kernel: per-kernel time split and the
+    # dominant kernel.
+    per_kind = {}
+    for kind, ms in run_logged(0xFF, 1, launches_per_step):
+        per_kind.setdefault(kind, []).append(ms)
+    split = {kd.KERNEL_NAMES[k]: round(sum(v), 4) for k, v in sorted(per_kind.items())}
+    dom = max(per_kind, key=lambda k: sum(per_kind[k]))
+    log(f"per-kernel ms in one step: {split}; dominant {kd.KERNEL_NAMES[dom]}")
+
+    # Timed region: K steps between full synchronisations of both runtimes;
+    # the dominant kernel's launches are bracketed by events on the stream.
+    cap = n_chunks * args.steps
+    starts = [hip.Event() for _ in range(cap)]
+    ends = [hip.Event() for _ in range(cap)]
+    arr_s = (ctypes.c_void_p * cap)(*[e.value for e in starts])
+    arr_e = (ctypes.c_void_p * cap)(*[e.value for e in ends])
+    kinds = (ctypes.c_int32 * cap)()
+    count = ctypes.c_int32(0)
+    kd.kd_set_launch_log(1 << dom, arr_s, arr_e, kinds, cap, ctypes.byref(count))
+    torch.cuda.synchronize()
+    hip.synchronize()
+    log(f"timing {args.steps} step(s)")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stream.synchronize()
+    t_end = time.perf_counter()
+    torch.cuda.synchronize()
+    kd.kd_set_launch_log(0, None, None, None, 0, None)
+    wall = t_end - t_start
+    ms_step = wall * 1e3 / args.steps
+    dom_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
+    dom_avg = sum(dom_ms) / len(dom_ms)
+
+    flops_step = 6.0 * T * d * V
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    tokens_s = T * args.steps / wall
+    flops_launch = 2.0 * chunk * d * V if dom in GEMM_KERNELS else None
+    if flops_launch is not None:
+        ach = flops_launch / (dom_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kd.KERNEL_NAMES[dom],
+                "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_for(kd.KERNEL_NAMES[dom], launches_per_step),
+                "launch_ms": round(dom_avg, 4), "launches": len(dom_ms),
+                "flops_per_launch": flops_launch}
+    else:
+        roof = {"bound": "hbm", "kernel": kd.KERNEL_NAMES[dom], "achieved": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None, "launch_ms": round(dom_avg, 4)}
+
+    # sanity: the loss is finite
+    lval = float(loss.item())
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": x.dtype,
+        "data": "synthetic",
+        "config": {"workload": x.name, "T": T, "d": d, "V": V, "K": K,
+                   "tau": x.tau, "chunk": chunk,
+                   "masked": 0 if x.mask is None else int(T - x.mask.sum()),
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "extra_hbm_bytes": ws_bytes,
+        "dense_extra_hbm_bytes": 8 * T * V,
+        "loss": lval,
+        "kernel_ms_one_step": split,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -131,6 +131,36 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
                        float *loss, float *row_loss, float *dH, float *dW,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Kernel ids for kd_set_launch_log (bit i of the mask selects id i). */
+enum {
+  KD_KERNEL_VALID_COUNT = 0, /* N = sum(mask), gradient and loss scales     */
+  KD_KERNEL_PREP_ROWS = 1,   /* teacher softmax over K, id sort, segments    */
+  KD_KERNEL_GEMM_LOGITS = 2, /* z = H_c W^T + per-segment softmax + gather   */
+  KD_KERNEL_LSE_FIX = 3,     /* row logsumexp, KL_t, teacher correction      */
+  KD_KERNEL_GEMM_DH = 4,     /* split-K partials of dH = G W                 */
+  KD_KERNEL_REDUCE_DH = 5,   /* ordered sum of the dH partials               */
+  KD_KERNEL_GEMM_DW = 6,     /* dW (+)= G^T H_c                              */
+  KD_KERNEL_FINAL_LOSS = 7   /* loss = tau^2/N sum_t row_loss                */
+};
+
+/*
+ * kd_set_launch_log -- measurement hook for profilers and benchmarks; it is
+ * not needed to compute the loss.  While installed on the calling thread,
+ * every kd_topk_kl_fwd_bwd launch of a kernel whose id bit is set in
+ * `kernel_mask` is bracketed by hipEventRecord(start_events[i]) and
+ * hipEventRecord(end_events[i]) on the call's stream, its id is stored in
+ * kinds[i] (if kinds is not NULL) and *count is incremented, for
+ * i = *count < capacity; launches beyond `capacity` are not recorded.
+ * start_events/end_events hold hipEvent_t handles (as void*) created by the
+ * caller in the same HIP runtime as this library; all arrays are host
+ * memory owned by the caller and must outlive the calls they log.  A zero
+ * `kernel_mask` (or NULL count) removes the hook.  Returns KD_OK, or
+ * KD_ERR_INVALID_ARG for a non-zero mask with NULL events or capacity < 0.
+ */
+int kd_set_launch_log(uint32_t kernel_mask, void *const *start_events,
+                      void *const *end_events, int32_t *kinds,
+                      int32_t capacity, int32_t *count);
+
 /* Static, NUL-terminated description of a status code.  For KD_ERR_HIP the
  * text also carries the HIP error string of the last failure on the calling
  * thread.  Never NULL. */

@@ -1,9 +1,14 @@
 """Python binding of libkdtopk.so, the MI355X fused chunked top-K KL loss.
 
 Argument marshalling only: every step of the loss runs in the HIP kernels of
-the C library (``include/kd_topk_kl.h``).  PyTorch provides device memory
-and the current stream.  There is no fallback: if the library is missing or
-cannot be loaded, every call raises.
+the C library (``include/kd_topk_kl.h``).  PyTorch provides device memory.
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+
+PyTorch-ROCm carries its own HIP runtime, separate from the one the library
+is linked against, so the binding orders the two by host synchronisation:
+torch's pending work is finished before the library call, and the library's
+stream is synchronised before results are handed back (``sync=True``).
 """
 from __future__ import annotations
 
@@ -13,7 +18,8 @@ import os
 __all__ = [
     "KD_F32", "KD_BF16", "KD_FLAG_ACCUMULATE_DW", "KD_MAX_K", "LIB_PATH",
     "KdError", "load_library", "kd_topk_kl_workspace_size",
-    "kd_topk_kl_fwd_bwd", "kd_status_string", "EXPORTED_SYMBOLS",
+    "kd_topk_kl_fwd_bwd", "kd_status_string", "kd_set_launch_log",
+    "EXPORTED_SYMBOLS", "KERNEL_NAMES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
@@ -23,7 +29,10 @@ KD_OK, KD_ERR_INVALID_ARG, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP = ra
 KD_FLAG_ACCUMULATE_DW = 1
 KD_MAX_K = 1024
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
-                    "kd_status_string")
+                    "kd_status_string", "kd_set_launch_log")
+# Kernel ids of the launch log (KD_KERNEL_* in the header).
+KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
+                "gemm_dh", "reduce_dh", "gemm_dw", "final_loss")
 
 _lib = None
 
@@ -57,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.kd_topk_kl_fwd_bwd.restype = c.c_int
     lib.kd_status_string.argtypes = [c.c_int]
     lib.kd_status_string.restype = c.c_char_p
+    lib.kd_set_launch_log.argtypes = [
+        c.c_uint32, c.POINTER(c.c_void_p), c.POINTER(c.c_void_p),
+        c.POINTER(c.c_int32), c.c_int32, c.POINTER(c.c_int32)]
+    lib.kd_set_launch_log.restype = c.c_int
     _lib = lib
     return lib
 
@@ -79,6 +92,16 @@ def kd_topk_kl_workspace_size(T, d, V, K, chunk, dtype) -> int:
     return out.value
 
 
+def kd_set_launch_log(kernel_mask, start_events, end_events, kinds, capacity,
+                      count):
+    """Install (or, with kernel_mask 0, remove) the per-thread launch log:
+    raw ctypes arrays of hipEvent_t handles, an int32 kinds array and an
+    int32 counter (see the C header)."""
+    _check(load_library().kd_set_launch_log(
+        int(kernel_mask), start_events, end_events, kinds, int(capacity),
+        count))
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -90,14 +113,19 @@ def _dtype_code(t):
 
 def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
                        chunk=None, flags=0, *, dW=None, row_loss=True,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, sync=True):
     """Loss, per-row KL, dH and dW of the top-K KL loss on the GPU.
 
     H [T,d] and W [V,d] (bf16 or fp32), topk_idx [T,K] int32, topk_logit
     [T,K] fp32 and mask [T] (uint8/bool or None) are CUDA tensors.  Outputs
     are allocated here (``dW`` may be passed in, e.g. with
-    KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW),
-    enqueued on ``stream`` (default: torch's current stream).
+    KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW).
+
+    ``stream`` is a stream handle of the library's HIP runtime
+    (``top_kl_loss_amd.hip.Stream().value``) or None for its null stream.
+    With ``sync=False`` the call returns as soon as the work is enqueued;
+    the caller must then keep every tensor alive and synchronise the stream
+    (``top_kl_loss_amd.hip.synchronize``) before torch touches the results.
     """
     import torch
     lib = load_library()
@@ -136,12 +164,15 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
         dW = torch.empty(V, d, **f32)
     elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
         raise ValueError("dW must be float32 [V, d]")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    from . import hip
+    torch.cuda.synchronize(dev)          # inputs written by torch are ready
+    hip.set_device(dev.index if dev.index is not None else 0)
     _check(lib.kd_topk_kl_fwd_bwd(
         H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
         topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
         T, d, V, K, float(tau), chunk, int(flags), loss.data_ptr(),
         rl.data_ptr() if rl is not None else None, dH.data_ptr(),
         dW.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
+    if sync:
+        hip.synchronize(stream)
     return loss, rl, dH, dW

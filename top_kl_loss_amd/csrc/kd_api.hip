@@ -15,6 +15,36 @@ namespace {
 
 thread_local char g_hip_msg[256] = "";
 
+struct LaunchLog {
+  uint32_t mask = 0;
+  void *const *start = nullptr;
+  void *const *end = nullptr;
+  int32_t *kinds = nullptr;
+  int32_t capacity = 0;
+  int32_t *count = nullptr;
+};
+thread_local LaunchLog g_log;
+
+// Runs `launch` (which enqueues one kernel of id `kind` on `s`), bracketed by
+// the caller's events when the launch log asks for it.
+template <class F>
+hipError_t logged(int kind, hipStream_t s, F &&launch) {
+  const bool rec = g_log.count && ((g_log.mask >> kind) & 1u) &&
+                   *g_log.count < g_log.capacity;
+  const int i = rec ? *g_log.count : 0;
+  if (rec) {
+    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(g_log.start[i]), s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (rec && e == hipSuccess) {
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(g_log.end[i]), s);
+    if (g_log.kinds) g_log.kinds[i] = kind;
+    ++*g_log.count;
+  }
+  return e;
+}
+
 struct Layout {
   int C, nseg, ldp, splits;
   size_t esize;
@@ -139,21 +169,43 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.dH = dH;
   a.dW = dW;
 
-  hipError_t e = kd::launch_valid_count(mask, (int)T, tau, scal, s);
+  hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {
+    return kd::launch_valid_count(mask, (int)T, tau, scal, s);
+  });
   if (e != hipSuccess) return hip_fail(e);
   for (int64_t c0 = 0; c0 < T; c0 += L.C) {
     a.c0 = c0;
     a.C = (int)(T - c0 < L.C ? T - c0 : L.C);
     a.dw_beta = (c0 > 0 || (flags & KD_FLAG_ACCUMULATE_DW)) ? 1 : 0;
-    if ((e = kd::launch_prep_rows(a, s)) != hipSuccess) return hip_fail(e);
-    if ((e = kd::launch_gemm_logits(a, bf16, s)) != hipSuccess) return hip_fail(e);
-    if ((e = kd::launch_lse_fix(a, bf16, s)) != hipSuccess) return hip_fail(e);
-    if ((e = kd::launch_gemm_dh(a, bf16, s)) != hipSuccess) return hip_fail(e);
-    if ((e = kd::launch_reduce_dh(a, s)) != hipSuccess) return hip_fail(e);
-    if ((e = kd::launch_gemm_dw(a, bf16, s)) != hipSuccess) return hip_fail(e);
+    if ((e = logged(KD_KERNEL_PREP_ROWS, s, [&] { return kd::launch_prep_rows(a, s); })) ||
+        (e = logged(KD_KERNEL_GEMM_LOGITS, s, [&] { return kd::launch_gemm_logits(a, bf16, s); })) ||
+        (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })) ||
+        (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
+        (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
+        (e = logged(KD_KERNEL_GEMM_DW, s, [&] { return kd::launch_gemm_dw(a, bf16, s); })))
+      return hip_fail(e);
   }
-  if ((e = kd::launch_final_loss(rl, (int)T, scal, loss, s)) != hipSuccess)
-    return hip_fail(e);
+  e = logged(KD_KERNEL_FINAL_LOSS, s, [&] {
+    return kd::launch_final_loss(rl, (int)T, scal, loss, s);
+  });
+  if (e != hipSuccess) return hip_fail(e);
+  return KD_OK;
+}
+
+int kd_set_launch_log(uint32_t kernel_mask, void *const *start_events,
+                      void *const *end_events, int32_t *kinds,
+                      int32_t capacity, int32_t *count) {
+  if (kernel_mask == 0 || count == nullptr) {
+    g_log = LaunchLog{};
+    return KD_OK;
+  }
+  if (!start_events || !end_events || capacity < 0) return KD_ERR_INVALID_ARG;
+  g_log.mask = kernel_mask;
+  g_log.start = start_events;
+  g_log.end = end_events;
+  g_log.kinds = kinds;
+  g_log.capacity = capacity;
+  g_log.count = count;
   return KD_OK;
 }
 

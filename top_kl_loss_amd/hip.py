@@ -1,0 +1,103 @@
+"""Minimal ctypes access to the HIP runtime that libkdtopk.so runs on.
+
+PyTorch-ROCm ships its own HIP runtime, so a process that uses both torch
+and libkdtopk.so holds two runtime instances: device memory is shared, but
+streams and events of one are unknown to the other.  Work of the library is
+therefore ordered against torch's by host synchronisation (see the binding),
+and timed with events of the library's own runtime (this module).
+"""
+from __future__ import annotations
+
+import ctypes
+
+_hip = None
+
+
+def runtime():
+    """The HIP runtime instance libkdtopk.so is linked against."""
+    global _hip
+    if _hip is not None:
+        return _hip
+    from . import load_library
+    load_library()  # makes sure the library's runtime is the loaded one
+    h = ctypes.CDLL("libamdhip64.so.7")
+    vp = ctypes.c_void_p
+    h.hipDeviceSynchronize.restype = ctypes.c_int
+    h.hipSetDevice.argtypes = [ctypes.c_int]
+    h.hipStreamSynchronize.argtypes = [vp]
+    h.hipStreamCreate.argtypes = [ctypes.POINTER(vp)]
+    h.hipStreamDestroy.argtypes = [vp]
+    h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+    h.hipEventRecord.argtypes = [vp, vp]
+    h.hipEventSynchronize.argtypes = [vp]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+    h.hipEventDestroy.argtypes = [vp]
+    h.hipGetErrorString.argtypes = [ctypes.c_int]
+    h.hipGetErrorString.restype = ctypes.c_char_p
+    _hip = h
+    return h
+
+
+def check(err):
+    if err != 0:
+        msg = runtime().hipGetErrorString(err).decode()
+        raise RuntimeError(f"HIP error {err}: {msg}")
+
+
+def set_device(index: int):
+    check(runtime().hipSetDevice(int(index)))
+
+
+def synchronize(stream=None):
+    """Wait for `stream` of the library's runtime (None: whole device)."""
+    if stream is None:
+        check(runtime().hipDeviceSynchronize())
+    else:
+        check(runtime().hipStreamSynchronize(stream))
+
+
+class Stream:
+    """A default-priority stream of the library's runtime."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        check(runtime().hipStreamCreate(ctypes.byref(self.handle)))
+
+    @property
+    def value(self):
+        return self.handle.value
+
+    def synchronize(self):
+        synchronize(self.handle)
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipStreamDestroy(self.handle)
+
+
+class Event:
+    """A timing event of the library's runtime."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        check(runtime().hipEventCreate(ctypes.byref(self.handle)))
+
+    @property
+    def value(self):
+        return self.handle.value
+
+    def record(self, stream=None):
+        check(runtime().hipEventRecord(self.handle, stream))
+
+    def synchronize(self):
+        check(runtime().hipEventSynchronize(self.handle))
+
+    def elapsed_ms(self, end: "Event") -> float:
+        ms = ctypes.c_float(0.0)
+        check(runtime().hipEventElapsedTime(ctypes.byref(ms), self.handle,
+                                            end.handle))
+        return ms.value
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
