@@ -48,7 +48,7 @@ def test_workspace_size_scales_with_chunk_not_with_T():
     assert a < dense / 50
     assert a - b < 32768 * 4 * 2        # only O(T) scalars grow with T
     c = kd.kd_topk_kl_workspace_size(32768, 2880, 201088, 100, 2048, kd.KD_BF16)
-    assert 1.8 * a < c < 2.2 * a
+    assert 1.5 * a < c < 2.2 * a
     # chunk is clamped to T
     assert (kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 64, kd.KD_F32) <
             kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 10 ** 6, kd.KD_F32)

@@ -123,3 +123,28 @@ def test_repeat_is_bitwise_identical_and_accumulate_adds():
     # rounding of the per-slice additions
     err = float((c[3] - 2 * a[3]).abs().max())
     assert err <= 1e-6 * float(a[3].abs().max())
+
+
+def test_bf16_tuned_path_ragged_tails():
+    # d a multiple of 64 (tuned kernels) but not of the 256-wide tiles, V not
+    # a multiple of the segment, chunk not a multiple of the 256-row tile,
+    # T not a multiple of chunk, padding rows, tau != 1.
+    x = synth.make_case("bf16_tuned_ragged", case=30, T=700, d=320, V=3001,
+                        K=37, dtype="bf16", tau=1.3, mask_frac=0.1, chunk=300)
+    check_case(x)
+
+
+def test_bf16_tuned_path_reshift_and_small_slices():
+    rng = np.random.default_rng(7)
+    x = synth.make_case("bf16_tuned_reshift", case=31, T=130, d=64, V=1200,
+                        K=40, dtype="bf16", chunk=48)
+    W = (rng.standard_normal((1200, 64)) * 0.05).astype(np.float32)
+    W[7] = 0.0
+    W[7, 0] = 30.0
+    H = x.H.copy()
+    H[:, 0] = 5.0
+    x.W_bits = synth.f32_to_bf16_bits(W)
+    x.W = synth.bf16_bits_to_f32(x.W_bits)
+    x.H_bits = synth.f32_to_bf16_bits(H)
+    x.H = synth.bf16_bits_to_f32(x.H_bits)
+    check_case(x)

@@ -47,6 +47,7 @@ hipError_t logged(int kind, hipStream_t s, F &&launch) {
 
 struct Layout {
   int C, nseg, ldp, splits;
+  bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
       o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp;
@@ -73,7 +74,8 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.C = (int)(chunk < T ? chunk : T);
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
   L.ldp = L.nseg * kd::SEG;
-  L.splits = kd::dh_splits(L.C, (int)d, L.nseg);
+  L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, L.ldp);
+  L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast);
   L.esize = dtype == KD_BF16 ? 2 : 4;
   const size_t C = L.C, nseg = L.nseg;
   size_t o = 0;
@@ -168,6 +170,7 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.row_loss = rl;
   a.dH = dH;
   a.dW = dW;
+  a.fast = L.fast ? 1 : 0;
 
   hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {
     return kd::launch_valid_count(mask, (int)T, tau, scal, s);

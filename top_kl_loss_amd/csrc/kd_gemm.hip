@@ -445,7 +445,16 @@ hipError_t launch(K kern, int grid, int lds_bytes, const SliceArgs &a, hipStream
 
 }  // namespace
 
-int dh_splits(int C, int d, int nseg) {
+bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp) {
+  // byte offsets of the buffer loads, including one tile of rows past the
+  // end (those read as zero), must stay below 2^32
+  const int64_t lim = int64_t(1) << 32;
+  return bf16 && d % 64 == 0 && (V + 512) * d * 2 < lim &&
+         (C + 512) * ldp * 2 < lim && (C + 512) * d * 2 < lim;
+}
+
+int dh_splits(int C, int d, int nseg, bool fast) {
+  if (fast) return fast_dh_splits(C, d, nseg);
   const int tiles = ((C + DH_BM - 1) / DH_BM) * ((d + DH_BN - 1) / DH_BN);
   int s = (1024 + tiles - 1) / tiles;
   if (s < 1) s = 1;
@@ -454,6 +463,7 @@ int dh_splits(int C, int d, int nseg) {
 }
 
 hipError_t launch_gemm_logits(const SliceArgs &a, bool bf16, hipStream_t s) {
+  if (a.fast) return launch_fast_logits(a, s);
   using TL = Tile<G1_BM, G1_BN>;
   const int grid = ((a.C + TL::BM - 1) / TL::BM) * a.nseg;
   return bf16 ? launch(k_gemm_logits<uint16_t>, grid, TL::LDS, a, s)
@@ -461,6 +471,7 @@ hipError_t launch_gemm_logits(const SliceArgs &a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_gemm_dh(const SliceArgs &a, bool bf16, hipStream_t s) {
+  if (a.fast) return launch_fast_dh(a, s);
   using TL = Tile<DH_BM, DH_BN>;
   const int grid = ((a.C + TL::BM - 1) / TL::BM) * ((a.d + TL::BN - 1) / TL::BN) * a.splits;
   return bf16 ? launch(k_gemm_dh<uint16_t>, grid, TL::LDS, a, s)
@@ -468,6 +479,7 @@ hipError_t launch_gemm_dh(const SliceArgs &a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_gemm_dw(const SliceArgs &a, bool bf16, hipStream_t s) {
+  if (a.fast) return launch_fast_dw(a, s);
   using TL = Tile<DW_BM, DW_BN>;
   const int grid = ((a.V + TL::BM - 1) / TL::BM) * ((a.d + TL::BN - 1) / TL::BN);
   return bf16 ? launch(k_gemm_dw<uint16_t>, grid, TL::LDS, a, s)

@@ -61,6 +61,7 @@ struct SliceArgs {
   float *dH;         // [T, d]
   float *dW;         // [V, d]
   int dw_beta;       // 0: dW = G^T H, 1: dW += G^T H
+  int fast;          // use the tuned bf16 kernels
 };
 
 // Tile shapes of the three GEMMs (all use 256-thread workgroups).
@@ -68,7 +69,15 @@ constexpr int G1_BM = 128, G1_BN = SEG;   // logits:  C x V, K = d
 constexpr int DH_BM = 128, DH_BN = 128;   // dH:      C x d, K = V (split)
 constexpr int DW_BM = 128, DW_BN = 128;   // dW:      V x d, K = C
 
-int dh_splits(int C, int d, int nseg);
+// The tuned bf16 kernels (kd_gemm_fast.hip) need d % 64 == 0 and every
+// operand buffer below 4 GiB (32-bit buffer offsets); otherwise the generic
+// kernels (kd_gemm.hip) run.
+bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp);
+int dh_splits(int C, int d, int nseg, bool fast);
+int fast_dh_splits(int C, int d, int nseg);
+hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s);
+hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s);
+hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s);
 
 // Launch wrappers; each returns hipSuccess or the launch error.
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,
