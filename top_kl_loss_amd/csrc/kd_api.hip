@@ -50,7 +50,8 @@ struct Layout {
   bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
-      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp;
+      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht;
+  int ldh;
   size_t total;
 };
 
@@ -94,6 +95,8 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_lse = take(sizeof(float) * C);
   L.o_P = take(L.esize * C * (size_t)L.ldp);
   L.o_dhp = take(sizeof(float) * (size_t)L.splits * C * (size_t)d);
+  L.ldh = (int)((C + 63) / 64 * 64);
+  L.o_ht = take(L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0);
   L.total = o;
   return L;
 }
@@ -165,6 +168,8 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.lse = reinterpret_cast<float *>(ws + L.o_lse);
   a.P = ws + L.o_P;
   a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
+  a.Ht = reinterpret_cast<uint16_t *>(ws + L.o_ht);
+  a.ldh = L.ldh;
   a.dh_stride = (size_t)L.C * (size_t)d;
   a.splits = L.splits;
   a.row_loss = rl;

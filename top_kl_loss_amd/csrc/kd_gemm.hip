@@ -5,8 +5,8 @@
 //  dH:      dH_c = G W         (C x d, K = V)   split-K over vocabulary
 //  dW:      dW (+)= G^T H_c    (V x d, K = C)
 //
-// where G[t,v] = f[t, seg(v)] * P[t,v] is the logit gradient of the chunk
-// (f is computed by k_lse_fix).  This follows the pages' fused, chunked KL
+// where G (the logit gradient of the chunk, tau/N * mask * (p - q_scat)) is
+// written by k_lse_fix over the buffer the logits GEMM filled with P.  This follows the pages' fused, chunked KL
 // ("Making Knowledge Distillation Cheap Enough to Run at Scale", aipuls.nl,
 // section "Summary"; "Hugging Face and Multiverse Computing cut KD memory
 // costs", agent-gateway.com): only one slice's [C, V] block ever exists.
@@ -353,8 +353,8 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_logits(SliceArgs a) {
 
 // ---------------------------------------------------------------- dH GEMM
 // Tile (mt, nt, split): dH partial of rows m0.., columns n0.., over the
-// vocabulary segments of the split.  A = G = f * P (scaled while loading),
-// B = W with the vocabulary as contraction index (transposed while loading).
+// vocabulary segments of the split.  A = G, B = W with the vocabulary as
+// contraction index (transposed while loading).
 template <typename T>
 __global__ __launch_bounds__(NTHREADS) void k_gemm_dh(SliceArgs a) {
   using TL = Tile<DH_BM, DH_BN>;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_dh(SliceArgs a) {
   const int kbeg = sbeg * SEG, kend = send * SEG;
   const T *P = reinterpret_cast<const T *>(a.P);
   const T *W = reinterpret_cast<const T *>(a.W);
-  LoadK<T, TL::BM, true> la{P, a.ldp, a.C, kend, a.fseg, a.nseg};
+  LoadK<T, TL::BM, false> la{P, a.ldp, a.C, kend, nullptr, 0};
   LoadMN<T, TL::BN, false> lb{W, a.d, a.d, kend < a.V ? kend : a.V, nullptr, 0};
   f32x16 acc[TL::TM][TL::TN];
   mainloop<T, TL>(la, lb, m0, n0, kbeg, kend, lds, acc);
@@ -393,9 +393,8 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_dh(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dW GEMM
-// Tile (mt, nt): dW rows m0.. (vocabulary, inside one segment), columns
-// n0..; contraction over the slice's tokens.  A = P^T (transposed while
-// loading), B = H_c with row t scaled by f[t, seg] (so A*B = G^T H_c).
+// Tile (mt, nt): dW rows m0.. (vocabulary), columns n0..; contraction over
+// the slice's tokens.  A = G^T and B = H_c, both transposed while loading.
 template <typename T>
 __global__ __launch_bounds__(NTHREADS) void k_gemm_dw(SliceArgs a) {
   using TL = Tile<DW_BM, DW_BN>;
@@ -405,11 +404,10 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_dw(SliceArgs a) {
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int nt = tile % nnt, mt = tile / nnt;
   const int m0 = mt * TL::BM, n0 = nt * TL::BN;
-  const int seg = m0 / SEG;
   const T *P = reinterpret_cast<const T *>(a.P);
   const T *H = reinterpret_cast<const T *>(a.H) + a.c0 * a.d;
   LoadMN<T, TL::BM, false> la{P, a.ldp, a.ldp, a.C, nullptr, 0};
-  LoadMN<T, TL::BN, true> lb{H, a.d, a.d, a.C, a.fseg + seg, a.nseg};
+  LoadMN<T, TL::BN, false> lb{H, a.d, a.d, a.C, nullptr, 0};
   f32x16 acc[TL::TM][TL::TN];
   mainloop<T, TL>(la, lb, m0, n0, 0, a.C, lds, acc);
 

@@ -1,27 +1,30 @@
 // bf16 matrix-core GEMMs of the fused, chunked top-K KL loss, tuned for
-// gfx950 (used when d is a multiple of 64; other shapes and fp32 inputs take
-// the generic kernels of kd_gemm.hip, which compute the same thing).
+// gfx950 (used when d is a multiple of 64 and the operand buffers fit 32-bit
+// byte offsets; other shapes and fp32 inputs take the generic kernels of
+// kd_gemm.hip, which compute the same thing).
 //
-//  logits:  Z = H_c W^T        (C x V, K = d)   + softmax-statistics epilogue
-//  dH:      dH_c = G W         (C x d, K = V)   split-K over vocabulary
-//  dW:      dW (+)= G^T H_c    (V x d, K = C)
-// with G[t,v] = f[t, seg(v)] * P[t,v] (see kd_gemm.hip and k_lse_fix).
+//  logits:  Z = H_c W^T      (C x V, K = d)   + softmax-statistics epilogue
+//  dH:      dH_c = G W       (C x d, K = V)   split-K over the vocabulary
+//  dW:      dW (+)= G^T H_c  (V x d, K = C)   B operand = H_c^T (k_transpose_h)
+// G is the slice's logit gradient, written in bf16 over the P buffer by
+// k_lse_fix.
 //
-// Workgroup: 256 threads = 4 waves (2 x 2), tile 256 x 256, wave tile
-// 128 x 128 = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, fp32 accumulators.
-// One k-step is 64 bf16 of the contraction.  Operands are copied from HBM
-// straight into LDS with buffer_load_dwordx4 ... lds (no register staging);
-// reads past a buffer's end return zero, which pads row tails.  Two LDS
-// stages: the copy of step k+1 runs while step k's MFMAs execute.
+// Workgroup: 512 threads = 8 waves (2 per SIMD) as 2 (M) x 4 (N); tile
+// 256 x 256, wave tile 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators.  Two waves per SIMD let the hardware interleave
+// one wave's LDS/VMEM/VALU work with the other's MFMAs.  One k-step is 64
+// bf16 of the contraction, double-buffered in LDS (2 x 64 KiB).
 //
-// LDS layouts of one stage:
-//  * K-contiguous operand (rows of 64 k = 128 B): 16-byte chunk c of row r
-//    at r*128 + ((c ^ (r & 7)) * 16); fragments are read with ds_read_b128.
-//  * MN-contiguous operand (64 k-rows of 256 elements = 512 B): 32-byte unit
-//    u of k-row k at k*512 + (u ^ s(k)) * 32 with s(k) = (k & 7) ^ (k & 8 ? 4
-//    : 0); fragments are read with ds_read_b64_tr_b16, whose 16-lane groups
-//    return lane i the (i mod 4)-th 16-bit element of the rows addressed by
-//    lanes 4j + i/4 (j = 0..3), i.e. 4 consecutive k of one column.
+// Every operand tile sits in LDS as rows of 64 contraction elements (128
+// bytes), 16-byte chunk c of row r at r*128 + ((c ^ swz(r)) * 16) with
+// swz(r) = (r ^ (r >> 3)) & 7, and MFMA fragments are read with
+// ds_read_b128.  Operands whose contraction index is contiguous in memory are
+// copied HBM -> LDS with buffer_load_dwordx4 ... lds (reads past the buffer
+// end return zero); the others are read as 8 x 8 bf16 blocks into registers,
+// transposed with v_perm_b32 and written with ds_write_b128 (the swizzle
+// keeps both the transposed writes and the fragment reads conflict-free).
+#include <stdint.h>
+
 #include "kd_device.h"
 #include "kd_internal.h"
 
@@ -29,16 +32,16 @@ namespace kd {
 
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 512;
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WTM = 128, WTN = 128, TM = 4, TN = 4;
+constexpr int WN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
 constexpr int OP_BYTES = 256 * 128;          // one operand tile per stage
 constexpr int STAGE_BYTES = 2 * OP_BYTES;    // A then B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // 128 KiB
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_vptr;
-typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_ptr;
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_res(const void *base,
                                                            uint64_t bytes) {
@@ -47,102 +50,87 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_res(const void *base,
                                            (int)n, 0x00020000);
 }
 
-// 64 lanes x 16 bytes from `res` at per-lane byte offsets into LDS at
-// `lds_base` (wave-uniform) + lane * 16.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, char *lds_base,
-                                       uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_vptr)lds_base, 16, (int)voff, 0,
-                                           0, 0);
-}
-
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ int swz_mn(int k) { return (k & 7) ^ ((k & 8) ? 4 : 0); }
-
 // ------------------------------------------------------------- operand copy
-// K-contiguous operand: element (mn, k) at byte (mn * ld + k) * 2 of `res`.
-// Per k-step each wave issues 8 copies of 1 KiB (8 rows of 128 B).
+// K-contiguous operand, element (mn, k) at byte (mn * ld + k) * 2 of `res`,
+// copied by NW waves (index w among them), each issuing 32/NW instructions
+// of 1 KiB (8 rows x 128 B) per k-step.
+template <int NW>
 struct CopyK {
+  static constexpr int N = 32 / NW;
   __amdgpu_buffer_rsrc_t res;
-  uint32_t row_off[8];  // byte offset of this lane's row for copy n
-  int lds_off[8];       // wave-uniform LDS offset of copy n (relative)
+  uint32_t off[N];
+  int w;
   __device__ __forceinline__ void init(const void *base, uint64_t bytes, int64_t ld,
-                                       int mn0, int wave, int lane) {
+                                       int mn0, int w_, int lane) {
     res = make_res(base, bytes);
+    w = w_;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int p = (wave * 8 + n) * 64 + lane;   // 16-byte position in tile
+    for (int n = 0; n < N; ++n) {
+      const int p = (w * N + n) * 64 + lane;  // 16-byte position in the tile
       const int row = p >> 3, pc = p & 7;
-      const int lc = pc ^ (row & 7);
-      row_off[n] = (uint32_t)(((int64_t)(mn0 + row) * ld + lc * 8) * 2);
-      lds_off[n] = (wave * 8 + n) * 1024;
+      const int lc = pc ^ swz(row);
+      off[n] = (uint32_t)(((int64_t)(mn0 + row) * ld + lc * 8) * 2);
     }
   }
-  __device__ __forceinline__ void issue(char *lds_tile, int k0) {
+  __device__ __forceinline__ void issue(char *tile, int k0) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) copy16(res, lds_tile + lds_off[n], row_off[n] + k0 * 2);
+    for (int n = 0; n < N; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_vptr)(tile + (w * N + n) * 1024), 16,
+                                               (int)(off[n] + k0 * 2), 0, 0, 0);
   }
 };
 
-// MN-contiguous operand: element (mn, k) at byte (k * ld + mn) * 2 of `res`.
-// Per k-step each wave issues 8 copies of 1 KiB (2 k-rows of 512 B).
-struct CopyMN {
-  __amdgpu_buffer_rsrc_t res;
-  uint32_t off[8];
-  int lds_off[8];
+// MN-contiguous operand, element (mn, k) at base[k * ld + mn], through
+// registers: thread t (< 256) owns the 8 x 8 block (mn block t % 32, k block
+// t / 32) of the 256 x 64 tile; elements outside mn < mn_lim, k < k_lim are
+// zero.
+struct RegMN {
+  const uint16_t *base;
   int64_t ld;
-  __device__ __forceinline__ void init(const void *base, uint64_t bytes, int64_t ld_,
-                                       int mn0, int wave, int lane) {
-    res = make_res(base, bytes);
+  int mn, kb, mn_lim, k_lim;
+  u32x4 r[8];
+  __device__ __forceinline__ void init(const uint16_t *b, int64_t ld_, int mn0, int mn_lim_,
+                                       int k_lim_, int t) {
+    base = b;
     ld = ld_;
+    mn = mn0 + (t & 31) * 8;
+    kb = (t >> 5) * 8;
+    mn_lim = mn_lim_;
+    k_lim = k_lim_;
+  }
+  __device__ __forceinline__ void load(int k0) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int kr = 2 * (wave * 8 + n) + (lane >> 5);
-      const int c = lane & 31, u = c >> 1, h = c & 1;
-      const int lu = u ^ swz_mn(kr);
-      off[n] = (uint32_t)(((int64_t)kr * ld + mn0 + (lu * 2 + h) * 8) * 2);
-      lds_off[n] = (wave * 8 + n) * 1024;
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + kb + e;
+      r[e] = (k < k_lim && mn < mn_lim)
+                 ? *reinterpret_cast<const u32x4 *>(base + (int64_t)k * ld + mn)
+                 : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __device__ __forceinline__ void issue(char *lds_tile, int k0) {
-    const uint32_t kb = (uint32_t)((int64_t)k0 * ld * 2);
+  // 8 x 8 transpose of 16-bit values: row m of the result holds element m of
+  // each loaded row, i.e. 8 consecutive k of one mn.
+  __device__ __forceinline__ void store(char *tile, int t) {
+    const int row0 = (t & 31) * 8, ch = t >> 5;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) copy16(res, lds_tile + lds_off[n], off[n] + kb);
+    for (int m = 0; m < 8; ++m) {
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = r[2 * p][m >> 1], hi = r[2 * p + 1][m >> 1];
+        o[p] = (m & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                       : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+      const int row = row0 + m;
+      *reinterpret_cast<u32x4 *>(tile + row * 128 + ((ch ^ swz(row)) << 4)) = o;
+    }
   }
 };
 
-// --------------------------------------------------------- fragment reads
-// 8 consecutive k (16 bytes) of row `row`, k-group g, half h of a
-// K-contiguous tile.
-__device__ __forceinline__ u32x4 frag_k(const char *tile, int row, int g, int h) {
-  const int ch = (2 * g + h) ^ (row & 7);
-  return *reinterpret_cast<const u32x4 *>(tile + row * 128 + ch * 16);
-}
-
-// 8 consecutive k of column `col` (= col0 + lane % 32) for k-group g of an
-// MN-contiguous tile, via two transposing reads.
-__device__ __forceinline__ u32x4 frag_mn(const char *tile, int col0, int g, int lane) {
-  const int grp = lane >> 4, i = lane & 15;
-  const int kb = 16 * g + 8 * (grp >> 1) + (i >> 2);
-  const int c = col0 + 16 * (grp & 1) + 4 * (i & 3);
-  const int u = c >> 4, w = (c & 15) * 2;
-  const char *p0 = tile + kb * 512 + ((u ^ swz_mn(kb)) << 5) + w;
-  const char *p1 = tile + (kb + 4) * 512 + ((u ^ swz_mn(kb + 4)) << 5) + w;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p1));
-  u32x4 r;
-  r[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-  r[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-  r[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-  r[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-  return r;
-}
-
-__device__ __forceinline__ u32x4 scale8(u32x4 v, float s) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(bf16_lo(v[i]) * s, bf16_hi(v[i]) * s);
-  return r;
+// 8 consecutive k (16 bytes) of tile row `row`, k-group g, half h.
+__device__ __forceinline__ u32x4 frag(const char *tile, int row, int g, int h) {
+  return *reinterpret_cast<const u32x4 *>(tile + row * 128 + (((2 * g + h) ^ swz(row)) << 4));
 }
 
 __device__ __forceinline__ void mfma(f32x16 &acc, u32x4 a, u32x4 b) {
@@ -163,6 +151,31 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
+// One k-step on fragments double-buffered in registers: group g+1's
+// fragments are read from LDS while group g's MFMAs run.
+__device__ __forceinline__ void kstep(const char *ta, const char *tb, int ar, int br, int h,
+                                      f32x16 (&acc)[TM][TN]) {
+  u32x4 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = frag(ta, ar + i * 32, 0, h);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = frag(tb, br + j * 32, 0, h);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int c = g & 1;
+    if (g < 3) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = frag(ta, ar + i * 32, g + 1, h);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = frag(tb, br + j * 32, g + 1, h);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[c][i], fb[c][j]);
+  }
+}
+
 __device__ __forceinline__ int xcd_swizzle(int bid, int n) {
   constexpr int NX = 8;
   const int per = (n + NX - 1) / NX;
@@ -172,54 +185,71 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int n) {
 }
 
 // ------------------------------------------------------------ logits GEMM
-// A = H_c (K-contiguous), B = W (K-contiguous).  Epilogue as in kd_gemm.hip:
-// per row and segment the max of z/tau, P = exp(z/tau - max) in bf16, the
-// sum of P, and z at the row's teacher ids inside the segment.
+// A = H_c, B = W (both K-contiguous).  Epilogue per row and segment: max of
+// z/tau, P = exp(z/tau - max) in bf16, the sum of P, and z itself at the
+// row's teacher ids inside the segment (the student-logit gather).
 __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int nmt = (a.C + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int mt = tile % nmt, seg = tile / nmt;
   const int m0 = mt * BM, n0 = seg * SEG;
   const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
   const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  CopyK ca, cb;
+  CopyK<8> ca, cb;
   ca.init(H, (uint64_t)a.C * a.d * 2, a.d, m0, wave, lane);
   cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
+
+  // Teacher ids of tile row m0 + tid (tid < 256) inside this segment,
+  // fetched now so that their latency hides under the main loop: up to NHIT
+  // (column, slot) pairs; `more` marks rows with further ids.
+  constexpr int NHIT = 4;
+  int hit_col[NHIT], hit_slot[NHIT];
+  bool more = false;
+#pragma unroll
+  for (int q = 0; q < NHIT; ++q) hit_col[q] = -1;
+  if (tid < BM && m0 + tid < a.C) {
+    const int r = m0 + tid;
+    const int pos = a.first[(size_t)r * a.nseg + seg];
+    if (pos >= 0) {
+      const int32_t *sid = a.sid + (size_t)r * a.K;
+      const int32_t *sslot = a.sslot + (size_t)r * a.K;
+#pragma unroll
+      for (int q = 0; q < NHIT; ++q) {
+        const int p = pos + q;
+        const int id = p < a.K ? sid[p] : INT32_MAX;
+        if (id < n0 + SEG) {
+          hit_col[q] = id - n0;
+          hit_slot[q] = sslot[p];
+        }
+      }
+      if (pos + NHIT < a.K && sid[pos + NHIT] < n0 + SEG) more = true;
+    }
+  }
 
   f32x16 acc[TM][TN];
   zero_acc(acc);
   const int nk = a.d / BK;
+  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
   ca.issue(lds, 0);
   cb.issue(lds + OP_BYTES, 0);
   for (int ks = 0; ks < nk; ++ks) {
-    char *cur = lds + (ks & 1) * STAGE_BYTES;
+    const char *cur = lds + (ks & 1) * STAGE_BYTES;
+    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+    // the last step re-copies itself into the idle stage (never read)
+    const int kn = (ks + 1 < nk ? ks + 1 : ks) * BK;
     wait_vm0();
     __syncthreads();
-    if (ks + 1 < nk) {
-      char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-      ca.issue(nxt, (ks + 1) * BK);
-      cb.issue(nxt + OP_BYTES, (ks + 1) * BK);
-    }
-    const char *ta = cur, *tb = cur + OP_BYTES;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag_k(ta, wm * WTM + i * 32 + (lane & 31), g, lane >> 5);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag_k(tb, wn * WTN + j * 32 + (lane & 31), g, lane >> 5);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[i], fb[j]);
-    }
+    ca.issue(nxt, kn);
+    cb.issue(nxt + OP_BYTES, kn);
+    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
   }
+  wait_vm0();
   __syncthreads();
 
-  // Epilogue: stage one block-row per wave-row (64 rows x 256 columns).
+  // Epilogue: one block-row of every wave per pass (64 rows x 256 columns).
   constexpr int PITCH = BN + 4;
   constexpr int SROWS = 64, TPR = NT / SROWS, CPT = BN / TPR;
   float *stage = reinterpret_cast<float *>(lds);
@@ -253,7 +283,7 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const float p = v[c] == -INFINITY ? 0.f : exp2f((v[c] - mx) * LOG2E);
+      const float p = v[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((v[c] - mx) * LOG2E);
       v[c] = p;
       sum += p;
     }
@@ -270,14 +300,25 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
       if (part == 0) {
         a.mseg[(size_t)r * a.nseg + seg] = mx;
         a.sseg[(size_t)r * a.nseg + seg] = sum;
-        int pos = a.first[(size_t)r * a.nseg + seg];
-        if (pos >= 0) {
-          const int32_t *sid = a.sid + (size_t)r * a.K;
-          const int32_t *sslot = a.sslot + (size_t)r * a.K;
-          for (; pos < a.K; ++pos) {
-            const int id = sid[pos];
+      }
+    }
+    // Gather z at the teacher ids: thread tid (< 256) owns tile row tid,
+    // staged in this pass when its 32-row block is block-row tm.
+    if (tid < BM && ((tid >> 5) & 3) == tm) {
+      const int r_own = m0 + tid;
+      const int sr_own = (tid >> 7) * 32 + (tid & 31);
+      if (r_own < a.C) {
+        float *zg = a.zg + (size_t)r_own * a.K;
+#pragma unroll
+        for (int q = 0; q < NHIT; ++q)
+          if (hit_col[q] >= 0) zg[hit_slot[q]] = stage[sr_own * PITCH + hit_col[q]];
+        if (more) {
+          const int32_t *sid = a.sid + (size_t)r_own * a.K;
+          const int32_t *sslot = a.sslot + (size_t)r_own * a.K;
+          for (int p = a.first[(size_t)r_own * a.nseg + seg] + NHIT; p < a.K; ++p) {
+            const int id = sid[p];
             if (id >= n0 + SEG) break;
-            a.zg[(size_t)r * a.K + sslot[pos]] = stage[sr * PITCH + (id - n0)];
+            zg[sslot[p]] = stage[sr_own * PITCH + (id - n0)];
           }
         }
       }
@@ -287,12 +328,12 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dH GEMM
-// A = P (K-contiguous over the vocabulary), scaled on the fragment by
-// f[t, seg]; B = W (MN-contiguous: vocabulary rows, hidden columns).
+// A = G (K-contiguous over the vocabulary; copied by waves 4-7), B = W
+// (vocabulary rows, hidden columns: through registers by threads 0-255).
 __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int nmt = (a.C + BM - 1) / BM;
   const int nnt = (a.d + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -302,55 +343,37 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
-  const uint16_t *P = reinterpret_cast<const uint16_t *>(a.P);
-  const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  CopyK ca;
-  CopyMN cb;
-  ca.init(P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-  cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
+  const int kbeg = sbeg * SEG, kend = send * SEG;
+  const bool copier = wave >= 4;
+  CopyK<4> ca;
+  RegMN rb;
+  if (copier)
+    ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave - 4, lane);
+  else
+    rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
 
   f32x16 acc[TM][TN];
   zero_acc(acc);
-  const int kbeg = sbeg * SEG;
-  const int nk = (send - sbeg) * (SEG / BK);
-  // rows of this lane's A blocks, for the per-(row, segment) scale
-  int arow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) arow[i] = m0 + wm * WTM + i * 32 + (lane & 31);
-  float fsc[TM];
-  ca.issue(lds, kbeg);
-  cb.issue(lds + OP_BYTES, kbeg);
+  const int nk = (kend - kbeg) / BK;
+  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  if (copier) {
+    ca.issue(lds, kbeg);
+  } else {
+    rb.load(kbeg);
+    rb.store(lds + OP_BYTES, tid);
+  }
   for (int ks = 0; ks < nk; ++ks) {
-    const int k0 = kbeg + ks * BK;
-    if ((ks & (SEG / BK - 1)) == 0) {
-      const int sg = k0 / SEG;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fsc[i] = arow[i] < a.C ? a.fseg[(size_t)arow[i] * a.nseg + sg] : 0.f;
-    }
-    char *cur = lds + (ks & 1) * STAGE_BYTES;
+    const char *cur = lds + (ks & 1) * STAGE_BYTES;
+    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+    const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
     wait_vm0();
     __syncthreads();
-    if (ks + 1 < nk) {
-      char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-      ca.issue(nxt, k0 + BK);
-      cb.issue(nxt + OP_BYTES, k0 + BK);
-    }
-    const char *ta = cur, *tb = cur + OP_BYTES;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = scale8(frag_k(ta, wm * WTM + i * 32 + (lane & 31), g, lane >> 5), fsc[i]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag_mn(tb, wn * WTN + j * 32, g, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[i], fb[j]);
-    }
+    if (copier) ca.issue(nxt, kn);
+    else rb.load(kn);
+    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+    if (!copier) rb.store(nxt + OP_BYTES, tid);
   }
+  wait_vm0();
 
   float *out = a.dh_part + (size_t)split * a.dh_stride;
 #pragma unroll
@@ -367,80 +390,46 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dW GEMM
-// A = P^T (MN-contiguous: token rows, vocabulary columns), B = H_c
-// (MN-contiguous: token rows, hidden columns) with token row t scaled by
-// f[t, seg] while it passes through registers.
+// A = G^T (token rows, vocabulary columns: through registers by threads
+// 0-255), B = H_c^T (K-contiguous over tokens; copied by waves 4-7).
 __global__ __launch_bounds__(NT, 1) void k_fast_dw(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int nnt = (a.d + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int nt = tile % nnt, mt = tile / nnt;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int seg = m0 / SEG;
-  const uint16_t *P = reinterpret_cast<const uint16_t *>(a.P);
-  const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
-  CopyMN ca;
-  ca.init(P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-
-  // B through registers: thread covers k-rows kr = tid/32 + 8*n (n < 8),
-  // 16-byte chunk c = tid % 32 of the 512-byte row.
-  const int bc = tid & 31;
-  const int bcol = n0 + bc * 8;
-  u32x4 breg[8];
-  float bsc[8];
-  auto load_b = [&](int k0) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int t = k0 + (tid >> 5) + 8 * n;
-      const bool ok = t < a.C && bcol < a.d;
-      breg[n] = ok ? *reinterpret_cast<const u32x4 *>(H + (size_t)t * a.d + bcol)
-                   : u32x4{0u, 0u, 0u, 0u};
-      bsc[n] = t < a.C ? a.fseg[(size_t)t * a.nseg + seg] : 0.f;
-    }
-  };
-  auto store_b = [&](char *tile_b) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int kr = (tid >> 5) + 8 * n;
-      const int u = bc >> 1, h = bc & 1;
-      *reinterpret_cast<u32x4 *>(tile_b + kr * 512 + ((u ^ swz_mn(kr)) << 5) + h * 16) =
-          scale8(breg[n], bsc[n]);
-    }
-  };
+  const bool copier = wave >= 4;
+  CopyK<4> cb;
+  RegMN ra;
+  if (copier)
+    cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave - 4, lane);
+  else
+    ra.init(reinterpret_cast<const uint16_t *>(a.P), a.ldp, m0, a.ldp, a.C, tid);
 
   f32x16 acc[TM][TN];
   zero_acc(acc);
   const int nk = (a.C + BK - 1) / BK;
-  ca.issue(lds, 0);
-  load_b(0);
-  store_b(lds + OP_BYTES);
+  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  if (copier) {
+    cb.issue(lds + OP_BYTES, 0);
+  } else {
+    ra.load(0);
+    ra.store(lds, tid);
+  }
   for (int ks = 0; ks < nk; ++ks) {
-    char *cur = lds + (ks & 1) * STAGE_BYTES;
+    const char *cur = lds + (ks & 1) * STAGE_BYTES;
+    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+    const int kn = (ks + 1 < nk ? ks + 1 : ks) * BK;
     wait_vm0();
     __syncthreads();
-    const bool more = ks + 1 < nk;
-    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-    if (more) {
-      ca.issue(nxt, (ks + 1) * BK);
-      load_b((ks + 1) * BK);
-    }
-    const char *ta = cur, *tb = cur + OP_BYTES;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag_mn(ta, wm * WTM + i * 32, g, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag_mn(tb, wn * WTN + j * 32, g, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[i], fb[j]);
-    }
-    if (more) store_b(nxt + OP_BYTES);
+    if (copier) cb.issue(nxt + OP_BYTES, kn);
+    else ra.load(kn);
+    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+    if (!copier) ra.store(nxt, tid);
   }
+  wait_vm0();
 
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -452,10 +441,34 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dw(SliceArgs a) {
         const int row = m0 + wm * WTM + i * 32 + acc_row(e, lane);
         if (row < a.V && col < a.d) {
           float *p = a.dW + (size_t)row * a.d + col;
-          *p = a.dw_beta ? *p + acc[i][j][e] : acc[i][j][e];
+          // exactly one addition per element and slice, slices in stream
+          // order: the result does not depend on timing
+          if (a.dw_beta)
+            unsafeAtomicAdd(p, acc[i][j][e]);
+          else
+            *p = acc[i][j][e];
         }
       }
     }
+}
+
+// Ht[j, t] = H[c0 + t, j] for t < C, 0 for C <= t < ldh (bf16), through
+// 64 x 64 tiles in LDS.
+__global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
+  __shared__ uint16_t t_s[64][66];
+  const int t0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    const int t = t0 + r, j = j0 + c;
+    t_s[r][c] = (t < a.C && j < a.d) ? H[(size_t)t * a.d + j] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;  // r: hidden index, c: token
+    const int j = j0 + r, t = t0 + c;
+    if (j < a.d && t < a.ldh) a.Ht[(size_t)j * a.ldh + t] = t_s[c][r];
+  }
 }
 
 template <typename K>
@@ -489,6 +502,10 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
+  const dim3 tg((a.ldh + 63) / 64, (a.d + 63) / 64);
+  hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch(k_fast_dw, ((a.V + BM - 1) / BM) * ((a.d + BN - 1) / BN), a, s);
 }
 

@@ -52,8 +52,11 @@ struct SliceArgs {
   float *mseg;       // [Cmax, nseg] segment max of z/tau (shift)
   float *sseg;       // [Cmax, nseg] segment sum of exp(z/tau - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
+  uint16_t *Ht;      // [d, ldh] bf16 H_c^T (tuned path only)
+  int ldh;           // row pitch of Ht: Cmax rounded up to 64
   float *lse;        // [Cmax] row logsumexp of z/tau
-  void *P;           // [Cmax, ldp] shifted probabilities (element type)
+  void *P;           // [Cmax, ldp] shifted probabilities, then (after
+                     // k_lse_fix) the logit gradient G (element type)
   float *dh_part;    // [splits, Cmax, d] split-K partial sums of dH
   size_t dh_stride;  // elements between two partials (Cmax * d)
   int splits;

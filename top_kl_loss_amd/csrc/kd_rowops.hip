@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
 //  KL_t  = c_t + lse_t - sum_k q_k z_k / tau      (z_k gathered by the GEMM);
 //  P[t, id_k] -= q_k exp(lse_t - shift_j)          (teacher correction, so
 //        that f_j * P is exactly tau/N (p - q_scat) on segment j);
-//  f_j   = tau/N * mask_t * exp(shift_j - lse_t).
+//  f_j   = tau/N * mask_t * exp(shift_j - lse_t);
+//  G[t, v] = f_seg(v) * P[t, v]  written over P (= tau/N mask (p - q_scat)).
 // A segment holding teacher ids whose shift lies more than RESHIFT_NATS
 // below lse_t is first re-shifted to lse_t - RESHIFT_NATS.
 template <typename T>
@@ -190,6 +191,16 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   float *frow = a.fseg + (size_t)r * nseg;
   for (int j = lane; j < nseg; j += 64)
     frow[j] = gscale != 0.f ? gscale * exp2f((mrow[j] - lse) * LOG2E) : 0.f;
+  __threadfence_block();
+  // G row = f_seg * P row, in place: the logit gradient the dH and dW GEMMs
+  // consume (all zero for a padding row).
+  constexpr int E = Elem<T>::PER16B;
+  u32x4 *P16 = reinterpret_cast<u32x4 *>(P);
+  const int nchunk = a.ldp / E;
+  for (int c = lane; c < nchunk; c += 64) {
+    const float f = frow[(c * E) / SEG];
+    P16[c] = Elem<T>::scale(P16[c], f);
+  }
 }
 
 // dH rows of the slice = ordered sum of the split-K partials.
