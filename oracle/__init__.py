@@ -7,6 +7,7 @@ from .kd_oracle import (  # noqa: F401
     dw_rows,
     kd_topk_kl,
     log_softmax_rows,
+    loss_given_lse,
     row_lse,
     rows_loss_and_dh,
     scattered_teacher,

@@ -61,6 +61,7 @@ __all__ = [
     "rows_loss_and_dh",
     "dw_rows",
     "scattered_teacher",
+    "loss_given_lse",
 ]
 
 
@@ -239,3 +240,30 @@ def dw_rows(H, W, topk_idx, topk_logit, mask, tau, lse, v_rows):
         qs[:, j] = (q * hit).sum(axis=1)
     G = (p - qs) * (grad_scale * m)[:, None]     # [T, R]
     return G.T @ H
+
+
+def loss_given_lse(H, W, topk_idx, topk_logit, mask, tau, lse):
+    """Total loss and per-row KL from every row's student logsumexp.
+
+    KL_t = sum_k q[t,k] (log q[t,k] - (z[t, idx[t,k]]/tau - lse_t)) needs the
+    full-vocabulary normaliser (from ``row_lse``) and only the K student
+    logits at the teacher's ids, so a full-size loss can be evaluated without
+    the dense logits.  Same readings R1-R6 as ``kd_topk_kl``.
+    Returns (loss, row_loss = mask * KL).
+    """
+    H = _f64(H)
+    tau = float(tau)
+    T = H.shape[0]
+    m = _mask_vector(mask, T)
+    n_valid = m.sum()
+    q, log_q = teacher_distribution(topk_logit, tau)
+    ids = np.asarray(topk_idx, dtype=np.int64)
+    z_at = np.empty(ids.shape)
+    for r0 in range(0, T, 1024):
+        Wg = _f64(W)[ids[r0:r0 + 1024]]                  # [R, K, d]
+        z_at[r0:r0 + 1024] = np.einsum("rd,rkd->rk", H[r0:r0 + 1024], Wg)
+    log_p_at = z_at / tau - _f64(lse)[:, None]
+    kl = (q * (log_q - log_p_at)).sum(axis=1)
+    row_loss = m * kl
+    loss = tau * tau * row_loss.sum() / n_valid if n_valid > 0 else 0.0
+    return loss, row_loss

@@ -1,0 +1,139 @@
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark times.  The oracle cannot afford the dense fp64 forward and
+backward at these sizes, so it checks what it can compute one by one:
+
+* the exact total loss and every row's KL where the full-vocabulary
+  logsumexp of every row is affordable (T = 4096), plus sampled dW rows;
+* sampled rows' KL and dH rows everywhere (each needs only that row and the
+  valid-token count);
+* identities that hold at any size: sum_v dW[v,:] = 0 (every logit-gradient
+  row sums to zero), <dH, H> = <dW, W> (both equal sum G*z), padding rows
+  get no gradient, and invariance to the slice size.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kd_oracle as orc
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _sample_rows(x, extra=()):
+    rng = np.random.default_rng(12345)
+    rows = set(int(r) for r in rng.choice(x.T, size=10, replace=False))
+    rows |= {0, x.T - 1, *extra}
+    if x.mask is not None:
+        rows |= set(int(r) for r in np.flatnonzero(x.mask == 0)[:2])
+    return np.array(sorted(r for r in rows if 0 <= r < x.T))
+
+
+def _check_rows(x, rl, dH, rows):
+    o_rl, o_dh = orc.rows_loss_and_dh(
+        x.H[rows], x.W, x.topk_idx[rows], x.topk_logit[rows],
+        None if x.mask is None else x.mask[rows], x.tau, x.n_valid)
+    g_rl = G.to_np(rl)[rows]
+    g_dh = G.to_np(dH[rows])
+    G.assert_grad_close(g_rl, o_rl, x.dtype, "sampled row_loss")
+    G.assert_grad_close(g_dh, o_dh, x.dtype, "sampled dH rows")
+    if x.mask is not None:
+        pad = x.mask[rows] == 0
+        assert np.all(g_dh[pad] == 0.0) and np.all(g_rl[pad] == 0.0)
+
+
+def _check_identities(x, dev, dH, dW):
+    import torch
+    dWd = dW.double()
+    colsum = dWd.sum(0).abs()
+    colabs = dWd.abs().sum(0)
+    ratio = float((colsum / colabs.clamp_min(1e-30)).max())
+    assert ratio <= 1e-3, f"sum_v dW not ~0: {ratio:.2e}"
+    Hd = dev["H"].double()
+    Wd = dev["W"].double()
+    a = float((dH.double() * Hd).sum())
+    b = float((dWd * Wd).sum())
+    scale = float((dH.double() * Hd).abs().sum())
+    assert abs(a - b) <= 1e-3 * scale, f"<dH,H>={a} <dW,W>={b}"
+    del Hd, Wd, dWd
+    torch.cuda.empty_cache()
+
+
+def test_t4k_exact_loss_all_rows_and_sampled_gradients():
+    x = synth.workload("t4k", teacher_device="cuda")
+    _say(f"t4k: T={x.T} d={x.d} V={x.V} chunk={x.chunk}")
+    dev = G.to_device(x)
+    loss, rl, dH, dW = G.run(dev, x.tau, x.chunk)
+    lse = orc.row_lse(x.H, x.W, x.tau, rows_per_block=512)
+    o_loss, o_rl = orc.loss_given_lse(x.H, x.W, x.topk_idx, x.topk_logit,
+                                      x.mask, x.tau, lse)
+    G.assert_loss_close(float(loss.item()), o_loss, x.dtype)
+    G.assert_grad_close(G.to_np(rl), o_rl, x.dtype, "row_loss (all rows)")
+    rows = _sample_rows(x, extra=(1023, 1024, 2047, 2048))
+    _check_rows(x, rl, dH, rows)
+    vs = np.unique(np.concatenate([x.topk_idx[0, :3], x.topk_idx[4095, :2],
+                                   [0, 1, 201087, 100000]]))
+    o_dw = orc.dw_rows(x.H, x.W, x.topk_idx, x.topk_logit, x.mask, x.tau,
+                       lse, vs)
+    G.assert_grad_close(G.to_np(dW[vs]), o_dw, x.dtype, "sampled dW rows")
+    _check_identities(x, dev, dH, dW)
+
+
+def test_t8k_masked_sampled_rows_and_identities():
+    x = synth.workload("t8k", teacher_device="cuda")
+    assert x.mask is not None and x.T - x.mask.sum() == 410
+    _say(f"t8k: T={x.T} masked={x.T - x.n_valid} chunk={x.chunk}")
+    dev = G.to_device(x)
+    loss, rl, dH, dW = G.run(dev, x.tau, x.chunk)
+    rows = _sample_rows(x, extra=(1023, 1024, 8191))
+    _check_rows(x, rl, dH, rows)
+    # the loss is tau^2/N times the sum of the per-row KL the library reports
+    tot = float(rl.double().sum()) * x.tau ** 2 / x.n_valid
+    assert abs(float(loss.item()) - tot) <= 1e-5 * abs(tot)
+    _check_identities(x, dev, dH, dW)
+
+
+def test_t32k_bench_configuration():
+    # T = 32768 at the slice size bench.py times
+    x = synth.workload("t32k", teacher_device="cuda")
+    _say(f"t32k: T={x.T} chunk={x.chunk}")
+    dev = G.to_device(x)
+    loss, rl, dH, dW = G.run(dev, x.tau, x.chunk)
+    rows = _sample_rows(x, extra=(x.chunk - 1, x.chunk, 3 * x.chunk + 5))
+    _check_rows(x, rl, dH, rows)
+    tot = float(rl.double().sum()) * x.tau ** 2 / x.n_valid
+    assert abs(float(loss.item()) - tot) <= 1e-5 * abs(tot)
+    _check_identities(x, dev, dH, dW)
+
+
+def test_t32k_d4096_chunk_sweep():
+    # d = 4096, V = 151936, tau = 2, 15% padding; slice sizes 512 ... 4096
+    import torch
+    x = synth.workload("t32k_d4096", teacher_device="cuda")
+    assert x.T - x.mask.sum() == 4915
+    dev = G.to_device(x)
+    ref = None
+    for c in synth.CHUNK_SWEEP["t32k_d4096"]:
+        _say(f"t32k_d4096: chunk={c}")
+        loss, rl, dH, dW = G.run(dev, x.tau, c)
+        if c == 1024:
+            rows = _sample_rows(x, extra=(1023, 1024, 30000))
+            _check_rows(x, rl, dH, rows)
+            _check_identities(x, dev, dH, dW)
+        if ref is None:
+            ref = (float(loss.item()), rl.clone(), dH.clone(), dW.clone())
+        else:
+            assert abs(float(loss.item()) - ref[0]) <= 1e-5 * abs(ref[0])
+            for name, g, o in (("row_loss", rl, ref[1]), ("dH", dH, ref[2]),
+                               ("dW", dW, ref[3])):
+                err = float((g - o).abs().max()) / float(o.abs().max())
+                assert err <= 2e-3, f"chunk {c}: {name} differs by {err:.2e}"
+        del loss, rl, dH, dW
+        torch.cuda.empty_cache()
