@@ -77,11 +77,13 @@ def cpu_baseline(x, target_s):
                        x.tau, chunk=R)
         return time.perf_counter() - t0
 
-    R = 8
-    dt = run(R)
-    per = dt / R
-    R = int(max(8, min(x.T, 2048, target_s / max(per, 1e-9))))
-    log(f"cpu baseline: oracle on {R} tokens (~{per * R:.0f} s)")
+    # the oracle has a fixed cost (upcasting W) plus a per-token cost
+    t8 = run(8)
+    t32 = run(32)
+    per = max((t32 - t8) / 24, 1e-6)
+    fixed = max(t8 - 8 * per, 0.0)
+    R = int(max(32, min(x.T, 4096, (target_s - fixed) / per)))
+    log(f"cpu baseline: oracle on {R} tokens (~{fixed + per * R:.0f} s)")
     dt = run(R)
     return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
@@ -99,6 +101,10 @@ def main():
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="before the timed region, copy BYTES device-to-device "
+                         "3 times (a reference kernel of known traffic for "
+                         "rocprofv3 counter runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -156,7 +162,7 @@ def main():
             raise RuntimeError(kd.kd_status_string(st))
 
     n_chunks = (T + chunk - 1) // chunk
-    launches_per_step = 2 + 6 * n_chunks
+    launches_per_step = 2 + 7 * n_chunks
 
     def run_logged(mask_bits, n_steps, cap):
         """Run n_steps with the launch log on; returns [(kind, ms)]."""
@@ -177,6 +183,15 @@ def main():
         return [(kinds[i], starts[i].elapsed_ms(ends[i]))
                 for i in range(count.value)]
 
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 3 x {args.copy_calibration} bytes")
+
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         step()
@@ -185,7 +200,7 @@ def main():
     # One logged step over every kernel: per-kernel time split and the
     # dominant kernel.
     per_kind = {}
-    for kind, ms in run_logged(0xFF, 1, launches_per_step):
+    for kind, ms in run_logged(0x1FF, 1, launches_per_step):
         per_kind.setdefault(kind, []).append(ms)
     split = {kd.KERNEL_NAMES[k]: round(sum(v), 4) for k, v in sorted(per_kind.items())}
     dom = max(per_kind, key=lambda k: sum(per_kind[k]))

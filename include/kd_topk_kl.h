@@ -30,7 +30,8 @@
  * ---------------------------------
  * - All tensors are dense, row-major, contiguous, in device memory of the
  *   current HIP device; the caller allocates and owns every buffer.  The
- *   library allocates nothing and keeps no state between calls.
+ *   library allocates nothing and keeps no state between calls (apart from
+ *   the optional, per-thread measurement hook kd_set_launch_log).
  * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *   the default stream).  Outputs are valid once that stream has
  *   synchronised.  No call synchronises the host.
@@ -140,7 +141,8 @@ enum {
   KD_KERNEL_GEMM_DH = 4,     /* split-K partials of dH = G W                 */
   KD_KERNEL_REDUCE_DH = 5,   /* ordered sum of the dH partials               */
   KD_KERNEL_GEMM_DW = 6,     /* dW (+)= G^T H_c                              */
-  KD_KERNEL_FINAL_LOSS = 7   /* loss = tau^2/N sum_t row_loss                */
+  KD_KERNEL_FINAL_LOSS = 7,  /* loss = tau^2/N sum_t row_loss                */
+  KD_KERNEL_TRANSPOSE_H = 8  /* H_c^T staging for the dW GEMM (bf16 path)    */
 };
 
 /*

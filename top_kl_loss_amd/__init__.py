@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log")
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
-                "gemm_dh", "reduce_dh", "gemm_dw", "final_loss")
+                "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h")
 
 _lib = None
 

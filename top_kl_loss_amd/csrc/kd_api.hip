@@ -190,6 +190,7 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
         (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
+        (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DW, s, [&] { return kd::launch_gemm_dw(a, bf16, s); })))
       return hip_fail(e);
   }

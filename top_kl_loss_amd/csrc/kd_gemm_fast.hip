@@ -501,11 +501,14 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
   return launch(k_fast_dh, ((a.C + BM - 1) / BM) * ((a.d + BN - 1) / BN) * a.splits, a, s);
 }
 
-hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
+hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
+  if (!a.fast) return hipSuccess;
   const dim3 tg((a.ldh + 63) / 64, (a.d + 63) / 64);
   hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
   return launch(k_fast_dw, ((a.V + BM - 1) / BM) * ((a.d + BN - 1) / BN), a, s);
 }
 

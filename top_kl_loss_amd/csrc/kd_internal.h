@@ -81,6 +81,8 @@ int fast_dh_splits(int C, int d, int nseg);
 hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s);
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s);
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s);
+// H_c^T for the tuned dW GEMM (no-op on the generic path).
+hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s);
 
 // Launch wrappers; each returns hipSuccess or the launch error.
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,
