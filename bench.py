@@ -162,7 +162,7 @@ def main():
             raise RuntimeError(kd.kd_status_string(st))
 
     n_chunks = (T + chunk - 1) // chunk
-    launches_per_step = 2 + 7 * n_chunks
+    launches_per_step = 3 + 8 * n_chunks
 
     def run_logged(mask_bits, n_steps, cap):
         """Run n_steps with the launch log on; returns [(kind, ms)]."""
@@ -200,7 +200,7 @@ def main():
     # One logged step over every kernel: per-kernel time split and the
     # dominant kernel.
     per_kind = {}
-    for kind, ms in run_logged(0x1FF, 1, launches_per_step):
+    for kind, ms in run_logged(0x7FF, 1, launches_per_step):
         per_kind.setdefault(kind, []).append(ms)
     split = {kd.KERNEL_NAMES[k]: round(sum(v), 4) for k, v in sorted(per_kind.items())}
     dom = max(per_kind, key=lambda k: sum(per_kind[k]))

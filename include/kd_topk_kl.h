@@ -142,7 +142,9 @@ enum {
   KD_KERNEL_REDUCE_DH = 5,   /* ordered sum of the dH partials               */
   KD_KERNEL_GEMM_DW = 6,     /* dW (+)= G^T H_c                              */
   KD_KERNEL_FINAL_LOSS = 7,  /* loss = tau^2/N sum_t row_loss                */
-  KD_KERNEL_TRANSPOSE_H = 8  /* H_c^T staging for the dW GEMM (bf16 path)    */
+  KD_KERNEL_TRANSPOSE_H = 8, /* H_c^T staging for the dW GEMM (bf16 path)    */
+  KD_KERNEL_SCALE_G = 9,     /* G = f P in place and G^T (bf16 path)         */
+  KD_KERNEL_TRANSPOSE_W = 10 /* W^T once per call (bf16 path, chunk >= d)    */
 };
 
 /*

@@ -148,3 +148,11 @@ def test_bf16_tuned_path_reshift_and_small_slices():
     x.H_bits = synth.f32_to_bf16_bits(H)
     x.H = synth.bf16_bits_to_f32(x.H_bits)
     check_case(x)
+
+
+def test_bf16_tuned_path_with_transposed_weight_copy():
+    # chunk >= d: the dH GEMM reads a W^T copy made once per call; V and T
+    # ragged, padding rows
+    x = synth.make_case("bf16_wt", case=32, T=600, d=192, V=3001, K=50,
+                        dtype="bf16", tau=1.1, mask_frac=0.05, chunk=256)
+    check_case(x)

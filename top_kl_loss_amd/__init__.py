@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log")
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
-                "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h")
+                "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
+                "scale_g", "transpose_w")
 
 _lib = None
 

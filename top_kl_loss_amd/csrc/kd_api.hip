@@ -50,7 +50,8 @@ struct Layout {
   bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
-      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht;
+      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt;
+  bool wt;
   int ldh;
   size_t total;
 };
@@ -97,6 +98,12 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_dhp = take(sizeof(float) * (size_t)L.splits * C * (size_t)d);
   L.ldh = (int)((C + 63) / 64 * 64);
   L.o_ht = take(L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0);
+  L.o_gt = take(L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0);
+  // A W^T copy (V x d bf16) lets the dH GEMM copy both operands by DMA; it is
+  // kept only when it is no larger than one slice's G (C >= d), so the extra
+  // memory stays bounded by a slice.
+  L.wt = L.fast && (int64_t)L.C >= d;
+  L.o_wt = take(L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0);
   L.total = o;
   return L;
 }
@@ -169,6 +176,8 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.P = ws + L.o_P;
   a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
   a.Ht = reinterpret_cast<uint16_t *>(ws + L.o_ht);
+  a.Gt = reinterpret_cast<uint16_t *>(ws + L.o_gt);
+  a.Wt = L.wt ? reinterpret_cast<uint16_t *>(ws + L.o_wt) : nullptr;
   a.ldh = L.ldh;
   a.dh_stride = (size_t)L.C * (size_t)d;
   a.splits = L.splits;
@@ -181,6 +190,10 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
     return kd::launch_valid_count(mask, (int)T, tau, scal, s);
   });
   if (e != hipSuccess) return hip_fail(e);
+  if (a.Wt) {
+    e = logged(KD_KERNEL_TRANSPOSE_W, s, [&] { return kd::launch_transpose_w(a, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   for (int64_t c0 = 0; c0 < T; c0 += L.C) {
     a.c0 = c0;
     a.C = (int)(T - c0 < L.C ? T - c0 : L.C);
@@ -188,6 +201,7 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
     if ((e = logged(KD_KERNEL_PREP_ROWS, s, [&] { return kd::launch_prep_rows(a, s); })) ||
         (e = logged(KD_KERNEL_GEMM_LOGITS, s, [&] { return kd::launch_gemm_logits(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })) ||
+        (a.fast && (e = logged(KD_KERNEL_SCALE_G, s, [&] { return kd::launch_scale_g(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
         (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))) ||

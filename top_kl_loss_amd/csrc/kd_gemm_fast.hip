@@ -5,9 +5,9 @@
 //
 //  logits:  Z = H_c W^T      (C x V, K = d)   + softmax-statistics epilogue
 //  dH:      dH_c = G W       (C x d, K = V)   split-K over the vocabulary
-//  dW:      dW (+)= G^T H_c  (V x d, K = C)   B operand = H_c^T (k_transpose_h)
-// G is the slice's logit gradient, written in bf16 over the P buffer by
-// k_lse_fix.
+//  dW:      dW (+)= G^T H_c  (V x d, K = C)   operands G^T and H_c^T
+// G is the slice's logit gradient: k_scale_g writes it in bf16 over the P
+// buffer and also writes G^T; k_transpose_h writes H_c^T.
 //
 // Workgroup: 512 threads = 8 waves (2 per SIMD) as 2 (M) x 4 (N); tile
 // 256 x 256, wave tile 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16
@@ -83,20 +83,21 @@ struct CopyK {
 };
 
 // MN-contiguous operand, element (mn, k) at base[k * ld + mn], through
-// registers: thread t (< 256) owns the 8 x 8 block (mn block t % 32, k block
-// t / 32) of the 256 x 64 tile; elements outside mn < mn_lim, k < k_lim are
-// zero.
-struct RegMN {
+// registers: thread t (of 512) owns the 8 (k) x 4 (mn) block (mn block
+// t % 64, k block t / 64) of the 256 x 64 tile; it reads 8 rows of 8 bytes,
+// transposes them with v_perm_b32 and writes 4 rows of 16 bytes (8
+// consecutive k of one mn).  Elements outside mn < mn_lim, k < k_lim are 0.
+struct RegMN4 {
   const uint16_t *base;
   int64_t ld;
   int mn, kb, mn_lim, k_lim;
-  u32x4 r[8];
+  uint32_t r[8][2];
   __device__ __forceinline__ void init(const uint16_t *b, int64_t ld_, int mn0, int mn_lim_,
                                        int k_lim_, int t) {
     base = b;
     ld = ld_;
-    mn = mn0 + (t & 31) * 8;
-    kb = (t >> 5) * 8;
+    mn = mn0 + (t & 63) * 4;
+    kb = (t >> 6) * 8;
     mn_lim = mn_lim_;
     k_lim = k_lim_;
   }
@@ -104,17 +105,19 @@ struct RegMN {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = k0 + kb + e;
-      r[e] = (k < k_lim && mn < mn_lim)
-                 ? *reinterpret_cast<const u32x4 *>(base + (int64_t)k * ld + mn)
-                 : u32x4{0u, 0u, 0u, 0u};
+      if (k < k_lim && mn < mn_lim) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(base + (int64_t)k * ld + mn);
+        r[e][0] = v.x;
+        r[e][1] = v.y;
+      } else {
+        r[e][0] = r[e][1] = 0u;
+      }
     }
   }
-  // 8 x 8 transpose of 16-bit values: row m of the result holds element m of
-  // each loaded row, i.e. 8 consecutive k of one mn.
   __device__ __forceinline__ void store(char *tile, int t) {
-    const int row0 = (t & 31) * 8, ch = t >> 5;
+    const int row0 = (t & 63) * 4, ch = t >> 6;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       u32x4 o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -152,14 +155,18 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
 }
 
 // One k-step on fragments double-buffered in registers: group g+1's
-// fragments are read from LDS while group g's MFMAs run.
+// fragments are read from LDS while group g's MFMAs run.  The scheduling
+// barriers pin the order (one MFMA, one fragment read, ...) that keeps the
+// matrix pipe fed; the compiler's own order serialises reads and MFMAs.
 __device__ __forceinline__ void kstep(const char *ta, const char *tb, int ar, int br, int h,
                                       f32x16 (&acc)[TM][TN]) {
+  constexpr int NRD = TM + TN;  // fragment reads per group
   u32x4 fa[2][TM], fb[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) fa[0][i] = frag(ta, ar + i * 32, 0, h);
 #pragma unroll
   for (int j = 0; j < TN; ++j) fb[0][j] = frag(tb, br + j * 32, 0, h);
+  __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int c = g & 1;
@@ -173,6 +180,16 @@ __device__ __forceinline__ void kstep(const char *ta, const char *tb, int ar, in
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[c][i], fb[c][j]);
+    if (g < 3) {
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NRD, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+    }
   }
 }
 
@@ -182,6 +199,18 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int n) {
   const int tall = n % NX == 0 ? NX : n % NX;
   const int x = bid % NX, local = bid / NX;
   return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
+}
+
+// Grouped tile order: tiles run in groups of GM consecutive M-tiles, the
+// M index fastest, then N, so the ~32 tiles an XCD runs at once form a
+// GM x (32/GM) block whose operand slices are shared through its L2.
+__device__ __forceinline__ void group_tile(int L, int nm, int nn, int gm_max, int &m, int &n) {
+  const int per = gm_max * nn;
+  const int first = (L / per) * gm_max;
+  const int gm = nm - first < gm_max ? nm - first : gm_max;
+  const int r = L % per;
+  m = first + r % gm;
+  n = r / gm;
 }
 
 // ------------------------------------------------------------ logits GEMM
@@ -194,7 +223,8 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int nmt = (a.C + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int mt = tile % nmt, seg = tile / nmt;
+  int mt, seg;
+  group_tile(tile, nmt, a.nseg, 4, mt, seg);
   const int m0 = mt * BM, n0 = seg * SEG;
   const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
   const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
@@ -328,8 +358,9 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dH GEMM
-// A = G (K-contiguous over the vocabulary; copied by waves 4-7), B = W
-// (vocabulary rows, hidden columns: through registers by threads 0-255).
+// A = G (K-contiguous over the vocabulary; copied by DMA).  B = W^T by DMA
+// when the call keeps a W^T copy, else W (vocabulary rows, hidden columns)
+// transposed through registers.
 __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -337,41 +368,53 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
   const int nmt = (a.C + BM - 1) / BM;
   const int nnt = (a.d + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nt = tile % nnt;
-  const int mt = (tile / nnt) % nmt;
   const int split = tile / (nnt * nmt);
+  int mt, nt;
+  group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
   const int kbeg = sbeg * SEG, kend = send * SEG;
-  const bool copier = wave >= 4;
-  CopyK<4> ca;
-  RegMN rb;
-  if (copier)
-    ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave - 4, lane);
-  else
-    rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
-
+  CopyK<8> ca;
+  ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
   f32x16 acc[TM][TN];
   zero_acc(acc);
   const int nk = (kend - kbeg) / BK;
   const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
-  if (copier) {
+  if (a.Wt) {
+    // B = W^T (hidden rows, vocabulary contiguous): both operands by DMA
+    CopyK<8> cb;
+    cb.init(a.Wt, (uint64_t)a.d * a.ldp * 2, a.ldp, n0, wave, lane);
     ca.issue(lds, kbeg);
+    cb.issue(lds + OP_BYTES, kbeg);
+    for (int ks = 0; ks < nk; ++ks) {
+      const char *cur = lds + (ks & 1) * STAGE_BYTES;
+      char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+      const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
+      wait_vm0();
+      __syncthreads();
+      ca.issue(nxt, kn);
+      cb.issue(nxt + OP_BYTES, kn);
+      kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+    }
   } else {
+    // B = W (vocabulary rows, hidden contiguous) through registers
+    RegMN4 rb;
+    rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
+    ca.issue(lds, kbeg);
     rb.load(kbeg);
     rb.store(lds + OP_BYTES, tid);
-  }
-  for (int ks = 0; ks < nk; ++ks) {
-    const char *cur = lds + (ks & 1) * STAGE_BYTES;
-    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-    const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
-    wait_vm0();
-    __syncthreads();
-    if (copier) ca.issue(nxt, kn);
-    else rb.load(kn);
-    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
-    if (!copier) rb.store(nxt + OP_BYTES, tid);
+    for (int ks = 0; ks < nk; ++ks) {
+      const char *cur = lds + (ks & 1) * STAGE_BYTES;
+      char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+      const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
+      wait_vm0();
+      __syncthreads();
+      ca.issue(nxt, kn);
+      rb.load(kn);
+      kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+      rb.store(nxt + OP_BYTES, tid);
+    }
   }
   wait_vm0();
 
@@ -390,44 +433,36 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dW GEMM
-// A = G^T (token rows, vocabulary columns: through registers by threads
-// 0-255), B = H_c^T (K-contiguous over tokens; copied by waves 4-7).
+// A = G^T, B = H_c^T (both K-contiguous over the slice's tokens; DMA).
 __global__ __launch_bounds__(NT, 1) void k_fast_dw(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int nnt = (a.d + BN - 1) / BN;
+  const int nmt = (a.V + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nt = tile % nnt, mt = tile / nnt;
+  int mt, nt;
+  group_tile(tile, nmt, nnt, 4, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const bool copier = wave >= 4;
-  CopyK<4> cb;
-  RegMN ra;
-  if (copier)
-    cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave - 4, lane);
-  else
-    ra.init(reinterpret_cast<const uint16_t *>(a.P), a.ldp, m0, a.ldp, a.C, tid);
+  CopyK<8> ca, cb;
+  ca.init(a.Gt, (uint64_t)a.ldp * a.ldh * 2, a.ldh, m0, wave, lane);
+  cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave, lane);
 
   f32x16 acc[TM][TN];
   zero_acc(acc);
   const int nk = (a.C + BK - 1) / BK;
   const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
-  if (copier) {
-    cb.issue(lds + OP_BYTES, 0);
-  } else {
-    ra.load(0);
-    ra.store(lds, tid);
-  }
+  ca.issue(lds, 0);
+  cb.issue(lds + OP_BYTES, 0);
   for (int ks = 0; ks < nk; ++ks) {
     const char *cur = lds + (ks & 1) * STAGE_BYTES;
     char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
     const int kn = (ks + 1 < nk ? ks + 1 : ks) * BK;
     wait_vm0();
     __syncthreads();
-    if (copier) cb.issue(nxt + OP_BYTES, kn);
-    else ra.load(kn);
+    ca.issue(nxt, kn);
+    cb.issue(nxt + OP_BYTES, kn);
     kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
-    if (!copier) ra.store(nxt, tid);
   }
   wait_vm0();
 
@@ -471,6 +506,58 @@ __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
   }
 }
 
+// Wt[j, v] = W[v, j] for v < V, 0 for V <= v < ldp, through 64 x 64 tiles.
+__global__ __launch_bounds__(256) void k_transpose_w(SliceArgs a) {
+  __shared__ uint16_t t_s[64][66];
+  const int v0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    const int v = v0 + r, j = j0 + c;
+    t_s[r][c] = (v < a.V && j < a.d) ? W[(size_t)v * a.d + j] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;  // r: hidden index, c: vocabulary
+    const int j = j0 + r, v = v0 + c;
+    if (j < a.d && v < a.ldp) a.Wt[(size_t)j * a.ldp + v] = t_s[c][r];
+  }
+}
+
+// G = f[t, seg] * P over one 64-row x 256-column (one segment) tile, written
+// in place, and G^T[v, t] through LDS; G^T columns t >= C are zero.
+__global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
+  __shared__ uint16_t g_s[64][256 + 8];
+  const int t0 = blockIdx.x * 64, seg = blockIdx.y, v0 = seg * SEG;
+  const int tid = threadIdx.x;
+  uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
+  const int c = tid & 31;            // 16-byte chunk of the 512-byte row
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 5) + 8 * i;
+    const int t = t0 + r;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (t < a.C) {
+      u32x4 *src = reinterpret_cast<u32x4 *>(P + (size_t)t * a.ldp + v0) + c;
+      v = Elem<uint16_t>::scale(*src, a.fseg[(size_t)t * a.nseg + seg]);
+      *src = v;
+    }
+    *reinterpret_cast<u32x4 *>(&g_s[r][c * 8]) = v;
+  }
+  __syncthreads();
+  // thread tid writes column v0 + tid: 64 tokens = 128 bytes
+  const int v = v0 + tid;
+  uint16_t *dst = a.Gt + (size_t)v * a.ldh + t0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      o[p] = uint32_t(g_s[q * 8 + 2 * p][tid]) | (uint32_t(g_s[q * 8 + 2 * p + 1][tid]) << 16);
+    if (t0 + q * 8 < a.ldh) reinterpret_cast<u32x4 *>(dst)[q] = o;
+  }
+}
+
 template <typename K>
 hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
@@ -505,6 +592,20 @@ hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
   const dim3 tg((a.ldh + 63) / 64, (a.d + 63) / 64);
   hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s) {
+  if (!a.Wt) return hipSuccess;
+  const dim3 g(a.ldp / 64, (a.d + 63) / 64);
+  hipLaunchKernelGGL(k_transpose_w, g, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s) {
+  if (!a.fast) return hipSuccess;
+  const dim3 g((a.ldh + 63) / 64, a.nseg);
+  hipLaunchKernelGGL(k_scale_g, g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ struct SliceArgs {
   float *sseg;       // [Cmax, nseg] segment sum of exp(z/tau - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
   uint16_t *Ht;      // [d, ldh] bf16 H_c^T (tuned path only)
+  uint16_t *Gt;      // [ldp, ldh] bf16 G^T (tuned path only)
+  uint16_t *Wt;      // [d, ldp] bf16 W^T (tuned path with C >= d), or null
   int ldh;           // row pitch of Ht: Cmax rounded up to 64
   float *lse;        // [Cmax] row logsumexp of z/tau
   void *P;           // [Cmax, ldp] shifted probabilities, then (after
@@ -83,6 +85,11 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s);
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s);
 // H_c^T for the tuned dW GEMM (no-op on the generic path).
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s);
+// Tuned path with a W^T buffer: W^T once per call (before the slices).
+hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s);
+// Tuned path: G = f_seg * P in place and G^T (no-op on the generic path,
+// where k_lse_fix scales P itself).
+hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s);
 
 // Launch wrappers; each returns hipSuccess or the launch error.
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,

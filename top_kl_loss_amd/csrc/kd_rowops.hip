@@ -191,6 +191,7 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   float *frow = a.fseg + (size_t)r * nseg;
   for (int j = lane; j < nseg; j += 64)
     frow[j] = gscale != 0.f ? gscale * exp2f((mrow[j] - lse) * LOG2E) : 0.f;
+  if (a.fast) return;  // k_scale_g forms G (and G^T) on the tuned path
   __threadfence_block();
   // G row = f_seg * P row, in place: the logit gradient the dH and dW GEMMs
   // consume (all zero for a padding row).
