@@ -545,16 +545,17 @@ __global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
     *reinterpret_cast<u32x4 *>(&g_s[r][c * 8]) = v;
   }
   __syncthreads();
-  // thread tid writes column v0 + tid: 64 tokens = 128 bytes
-  const int v = v0 + tid;
-  uint16_t *dst = a.Gt + (size_t)v * a.ldh + t0;
+  // G^T rows v0.. of this tile: 64 tokens = 128 bytes each, written by 8
+  // consecutive lanes (16 bytes each) so every store fills whole lines.
+  const int q = tid & 7;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int i = 0; i < 8; ++i) {
+    const int vr = (tid >> 3) + 32 * i;
     u32x4 o;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      o[p] = uint32_t(g_s[q * 8 + 2 * p][tid]) | (uint32_t(g_s[q * 8 + 2 * p + 1][tid]) << 16);
-    if (t0 + q * 8 < a.ldh) reinterpret_cast<u32x4 *>(dst)[q] = o;
+      o[p] = uint32_t(g_s[q * 8 + 2 * p][vr]) | (uint32_t(g_s[q * 8 + 2 * p + 1][vr]) << 16);
+    reinterpret_cast<u32x4 *>(a.Gt + (size_t)(v0 + vr) * a.ldh + t0)[q] = o;
   }
 }
 
