@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--op", choices=("loss", "teacher_topk"), default="loss",
+                    help="loss: kd_topk_kl_fwd_bwd (default); teacher_topk: "
+                         "kd_teacher_topk, the teacher cache build")
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -112,6 +115,9 @@ def main():
               f"path (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "teacher_topk":
+        return bench_teacher(args)
 
     import numpy as np
     import torch
@@ -270,6 +276,178 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+TEACHER_METRIC = ("tokens/s & TFLOP/s teacher top-100 cache build (LM-head GEMM + "
+                  "per-row top-K), T=32k V=201k; % bf16 MFMA peak")
+TK_KINDS = {11: "tk_sample", 12: "tk_theta", 13: "tk_filter", 14: "tk_select",
+            15: "tk_stream"}
+
+
+def cpu_baseline_teacher(x, K, target_s):
+    """The teacher-cache oracle, as it stands, on the first R rows."""
+    from oracle import teacher_topk as tko
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) \
+            if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+
+    def run(R):
+        t0 = time.perf_counter()
+        tko.teacher_topk_cache(x.H[:R], x.W, K)
+        return time.perf_counter() - t0
+
+    t4 = run(4)
+    t16 = run(16)
+    per = max((t16 - t4) / 12, 1e-6)
+    fixed = max(t4 - 4 * per, 0.0)
+    R = int(max(16, min(x.T, 4096, (target_s - fixed) / per)))
+    log(f"cpu baseline: teacher oracle on {R} rows (~{fixed + per * R:.0f} s)")
+    dt = run(R)
+    return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {R} of {x.T} rows of {x.name} (full d={x.d}, "
+                      f"V={x.V}, K={K}), fp64 NumPy matmul + per-row "
+                      f"lexsort; {dt:.1f} s wall"}
+
+
+def bench_teacher(args):
+    """One step = one kd_teacher_topk call over T = 32768 rows of a random
+    bf16 teacher (d = 2880, V = 201088, K = 100): the cache the loss reads."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+
+    torch.cuda.init()
+    lib = kd.load_library()
+    spec = synth.WORKLOADS[args.workload]
+    T, d, V, K = spec["T"], spec["d"], spec["V"], spec["K"]
+    chunk = args.chunk or 4096
+    log(f"generating teacher head for {args.workload}: T={T} d={d} V={V}")
+    t0 = time.perf_counter()
+    x = synth.teacher_head(f"{args.workload}_teacher", case=spec["case"], T=T,
+                           d=d, V=V, dtype=synth.BF16)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; K={K} chunk={chunk}")
+    dev = torch.device("cuda:0")
+    H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    ws_bytes = kd.kd_teacher_topk_workspace_size(T, d, V, K, chunk, kd.KD_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ids = torch.empty(T, K, dtype=torch.int32, device=dev)
+    vals = torch.empty(T, K, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    hip.set_device(0)
+    stream = hip.Stream()
+
+    def step():
+        st = lib.kd_teacher_topk(H.data_ptr(), W.data_ptr(), kd.KD_BF16, T, d,
+                                 V, K, chunk, ids.data_ptr(), vals.data_ptr(),
+                                 ws.data_ptr(), ws_bytes, stream.value)
+        if st != 0:
+            raise RuntimeError(kd.kd_status_string(st))
+
+    n_chunks = (T + chunk - 1) // chunk
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 3 x {args.copy_calibration} bytes")
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+
+    def logged(mask_bits, n_steps, cap):
+        starts = [hip.Event() for _ in range(cap)]
+        ends = [hip.Event() for _ in range(cap)]
+        arr_s = (ctypes.c_void_p * cap)(*[e.value for e in starts])
+        arr_e = (ctypes.c_void_p * cap)(*[e.value for e in ends])
+        kinds = (ctypes.c_int32 * cap)()
+        count = ctypes.c_int32(0)
+        kd.kd_set_launch_log(mask_bits, arr_s, arr_e, kinds, cap,
+                             ctypes.byref(count))
+        # the library reads arr_s / arr_e at every logged launch: the caller
+        # keeps them alive until the log is removed
+        return starts, ends, kinds, count, (arr_s, arr_e)
+
+    # one logged step over every kernel: the time split and the dominant one
+    s_, e_, k_, c_, keep = logged(0x1F << 11, 1, 5 * n_chunks)
+    step()
+    stream.synchronize()
+    kd.kd_set_launch_log(0, None, None, None, 0, None)
+    per_kind = {}
+    for i in range(c_.value):
+        per_kind.setdefault(k_[i], []).append(s_[i].elapsed_ms(e_[i]))
+    split = {TK_KINDS[k]: round(sum(v), 4) for k, v in sorted(per_kind.items())}
+    dom = max(per_kind, key=lambda k: sum(per_kind[k]))
+    log(f"per-kernel ms in one step: {split}; dominant {TK_KINDS[dom]}")
+
+    del keep
+    starts, ends, kinds, count, keep = logged(1 << dom, args.steps,
+                                              n_chunks * args.steps)
+    torch.cuda.synchronize()
+    hip.synchronize()
+    log(f"timing {args.steps} step(s)")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stream.synchronize()
+    t_end = time.perf_counter()
+    kd.kd_set_launch_log(0, None, None, None, 0, None)
+    del keep
+    wall = t_end - t_start
+    ms_step = wall * 1e3 / args.steps
+    dom_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
+    dom_avg = sum(dom_ms) / len(dom_ms)
+    tflops = 2.0 * T * d * V / (ms_step * 1e-3) / 1e12
+
+    # algorithmic work of the dominant kernel per launch
+    nseg = (V + 255) // 256
+    ns = min(32, nseg)
+    stride = 1 if nseg <= 32 else nseg // 32
+    cols = {11: ns * 256, 13: (nseg - ns) * 256}.get(dom)
+    if cols is not None:
+        flops_launch = 2.0 * chunk * d * cols
+        ach = flops_launch / (dom_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": TK_KINDS[dom], "achieved": round(ach, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_for(TK_KINDS[dom], None),
+                "launch_ms": round(dom_avg, 4), "launches": len(dom_ms),
+                "flops_per_launch": flops_launch}
+    else:
+        roof = {"bound": "hbm", "kernel": TK_KINDS[dom], "achieved": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None, "launch_ms": round(dom_avg, 4)}
+    got = ids.cpu().numpy()
+    assert np.all((got >= 0) & (got < V)), "ids out of range"
+    out = {
+        "metric": TEACHER_METRIC, "value": round(T * args.steps / wall, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": x.name, "T": T, "d": d, "V": V, "K": K,
+                   "chunk": chunk, "sampled_segments": ns,
+                   "sample_stride": stride, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "extra_hbm_bytes": ws_bytes,
+        "dense_logits_bytes": 4 * T * V,
+        "kernel_ms_one_step": split,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_teacher(x, K, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -144,20 +144,78 @@ enum {
   KD_KERNEL_FINAL_LOSS = 7,  /* loss = tau^2/N sum_t row_loss                */
   KD_KERNEL_TRANSPOSE_H = 8, /* H_c^T staging for the dW GEMM (bf16 path)    */
   KD_KERNEL_SCALE_G = 9,     /* G = f P in place and G^T (bf16 path)         */
-  KD_KERNEL_TRANSPOSE_W = 10 /* W^T once per call (bf16 path, chunk >= d)    */
+  KD_KERNEL_TRANSPOSE_W = 10, /* W^T once per call (bf16 path, chunk >= d)   */
+  /* kd_teacher_topk */
+  KD_KERNEL_TK_SAMPLE = 11,  /* logits of the sampled vocabulary segments    */
+  KD_KERNEL_TK_THETA = 12,   /* per-row threshold from the sampled logits    */
+  KD_KERNEL_TK_FILTER = 13,  /* logits of the other segments + candidates    */
+  KD_KERNEL_TK_SELECT = 14,  /* exact top-K of each row's candidates         */
+  KD_KERNEL_TK_STREAM = 15   /* row-streaming top-K (generic path, overflow) */
 };
+
+/* Largest supported K and hidden size of kd_teacher_topk. */
+#define KD_TOPK_MAX_K 256
+#define KD_TOPK_MAX_D 16384
+
+/*
+ * kd_teacher_topk_workspace_size -- bytes of scratch device memory needed by
+ * kd_teacher_topk for these sizes (per slice of `chunk` rows: the logits of
+ * 32 sampled vocabulary segments, 8192 candidate slots of 8 bytes and four
+ * words per row; bf16 with d % 64 == 0 only, otherwise 256 bytes).  It grows
+ * with chunk, never with T*V.  Arguments and return values as for
+ * kd_teacher_topk; `bytes_out` is a host pointer.
+ */
+int kd_teacher_topk_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                                   int32_t chunk, kd_dtype dtype,
+                                   size_t *bytes_out);
+
+/*
+ * kd_teacher_topk -- the offline teacher cache of the method: for every
+ * token row t, the K largest teacher logits z[t,v] = sum_j H[t,j] W[v,j]
+ * and their ids ("Making Knowledge Distillation Cheap Enough to Run at
+ * Scale", aipuls.nl, section "Summary": the teacher runs once and its
+ * top-100 logits per position are cached), computed slice by slice without
+ * the token-by-vocabulary logit matrix.
+ *
+ *   H           [T, d]  teacher final hidden states, dtype (bf16 or fp32)
+ *   W           [V, d]  teacher LM-head weight, dtype
+ *   T, d, V, K          sizes; T, d, V, K >= 1, K <= V, K <= KD_TOPK_MAX_K,
+ *                       d % 8 == 0, d <= KD_TOPK_MAX_D, T*d, V*d, T*K < 2^31
+ *   chunk       token rows per slice (>= 1; clamped to T)
+ *   topk_idx    [T, K]  int32 output: ids, by logit descending; equal
+ *                       logits are ordered by id ascending (-0 equals +0)
+ *   topk_logit  [T, K]  fp32 output: z at those ids (no temperature)
+ *   workspace   device scratch of at least kd_teacher_topk_workspace_size()
+ *               bytes, 256-byte aligned; contents on entry are ignored
+ *   stream      hipStream_t (as void*) on which all work is enqueued
+ *
+ * z is accumulated in fp32 from the inputs (bf16 products are exact).  With
+ * bf16 inputs and d % 64 == 0 it comes from the matrix-core GEMM; other
+ * inputs, and rows whose candidate count exceeds the 8192 slots (logits
+ * with strong structure against the sampled segments), are evaluated by a
+ * row-streaming kernel whose fp32 sums may differ from the GEMM's in the
+ * last bits.  Inputs must be finite (NaN logits have no defined rank).
+ * Returns KD_OK, KD_ERR_INVALID_ARG (NULL pointer, bad size, K > V),
+ * KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE or KD_ERR_HIP; checks run on the
+ * host before any HIP call.  Results are deterministic.
+ */
+int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
+                    int64_t d, int64_t V, int32_t K, int32_t chunk,
+                    int32_t *topk_idx, float *topk_logit, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * kd_set_launch_log -- measurement hook for profilers and benchmarks; it is
  * not needed to compute the loss.  While installed on the calling thread,
- * every kd_topk_kl_fwd_bwd launch of a kernel whose id bit is set in
+ * every launch of a kernel whose id bit is set in
  * `kernel_mask` is bracketed by hipEventRecord(start_events[i]) and
  * hipEventRecord(end_events[i]) on the call's stream, its id is stored in
  * kinds[i] (if kinds is not NULL) and *count is incremented, for
  * i = *count < capacity; launches beyond `capacity` are not recorded.
  * start_events/end_events hold hipEvent_t handles (as void*) created by the
  * caller in the same HIP runtime as this library; all arrays are host
- * memory owned by the caller and must outlive the calls they log.  A zero
+ * memory owned by the caller and must outlive the calls they log.  The hook
+ * applies to kd_topk_kl_fwd_bwd and kd_teacher_topk.  A zero
  * `kernel_mask` (or NULL count) removes the hook.  Returns KD_OK, or
  * KD_ERR_INVALID_ARG for a non-zero mask with NULL events or capacity < 0.
  */

@@ -13,3 +13,4 @@ from .kd_oracle import (  # noqa: F401
     scattered_teacher,
     teacher_distribution,
 )
+from .teacher_topk import teacher_logits, teacher_topk_cache  # noqa: F401

@@ -198,3 +198,71 @@ def workload(name, teacher_device=None, **overrides):
     spec = dict(WORKLOADS[name])
     spec.update(overrides)
     return make_case(name, teacher_device=teacher_device, **spec)
+
+
+# ------------------------------------------------ teacher top-K cache inputs
+@dataclasses.dataclass
+class TeacherHead:
+    """Teacher hidden states H [T, d] and LM head W [V, d] (exact fp32
+    values; bf16 bit patterns too when dtype is bf16)."""
+    name: str
+    T: int
+    d: int
+    V: int
+    dtype: str
+    H: np.ndarray
+    W: np.ndarray
+    H_bits: Optional[np.ndarray] = None
+    W_bits: Optional[np.ndarray] = None
+
+
+def _encode(name, H, W, dtype):
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    Hb = Wb = None
+    if dtype == BF16:
+        Hb, Wb = f32_to_bf16_bits(H), f32_to_bf16_bits(W)
+        H, W = bf16_bits_to_f32(Hb), bf16_bits_to_f32(Wb)
+    elif dtype != F32:
+        raise ValueError(dtype)
+    return TeacherHead(name=name, T=H.shape[0], d=H.shape[1], V=W.shape[0],
+                       dtype=dtype, H=H, W=W, H_bits=Hb, W_bits=Wb)
+
+
+def teacher_head(name="teacher", *, case, T, d, V, dtype=BF16, h_std=1.0):
+    """H ~ N(0, h_std^2) (stream 0) and W ~ N(0, 1/d) (stream 2, the
+    teacher head of the loss workloads)."""
+    return _encode(name, _normal(case, 0, (T, d), h_std),
+                   _normal(case, 2, (V, d), 1.0 / np.sqrt(d)), dtype)
+
+
+def teacher_head_integer(name="teacher_int", *, case, T, d, V, lo=-2, hi=2,
+                         zero_rows=(), dtype=BF16):
+    """Integer entries uniform in [lo, hi] (exact in bf16; with small d
+    every logit is an exact integer in fp32, so ties are frequent and
+    exact).  Rows listed in ``zero_rows`` of H are all zero."""
+    H = _rng(case, 0).integers(lo, hi + 1, size=(T, d)).astype(np.float32)
+    W = _rng(case, 2).integers(lo, hi + 1, size=(V, d)).astype(np.float32)
+    for r in zero_rows:
+        H[r] = 0.0
+    return _encode(name, H, W, dtype)
+
+
+def teacher_head_split(name="teacher_split", *, case, T, d, V, marked_segments,
+                       seg=256, dtype=BF16):
+    """Two families of vocabulary rows: ids in ``marked_segments`` (segment
+    width ``seg``) use only the first d/2 hidden dimensions, every other id
+    only the last d/2.  Even token rows use only the first half of H, odd
+    rows only the second half, so an even row has non-zero logits only on
+    the marked segments and an odd row only off them."""
+    H = _normal(case, 0, (T, d), 1.0)
+    W = _normal(case, 2, (V, d), 1.0 / np.sqrt(d / 2))
+    h = d // 2
+    marked = np.zeros(V, dtype=bool)
+    for s in marked_segments:
+        marked[s * seg:(s + 1) * seg] = True
+    W[marked, h:] = 0.0
+    W[~marked, :h] = 0.0
+    H[0::2, h:] = 0.0
+    H[1::2, :h] = 0.0
+    return _encode(name, H, W, dtype)

@@ -23,7 +23,7 @@ def declared_functions():
                                  src, flags=re.M)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_every_exported_entry_point():
     assert declared_functions() == sorted(kd.EXPORTED_SYMBOLS)
 
 
@@ -110,3 +110,60 @@ def _call(**kw):
 ])
 def test_fwd_bwd_rejects_before_any_hip_call(kw, code):
     assert _call(**kw) == code
+
+
+# ------------------------------------------------------ teacher top-K cache
+def test_teacher_workspace_is_bounded_by_the_slice():
+    a = kd.kd_teacher_topk_workspace_size(32768, 2880, 201088, 100, 4096, kd.KD_BF16)
+    b = kd.kd_teacher_topk_workspace_size(8192, 2880, 201088, 100, 4096, kd.KD_BF16)
+    assert a == b                         # nothing grows with T
+    per_row = 32 * 256 * 4 + 8192 * 8 + 16
+    assert 4096 * per_row <= a < 4096 * per_row + 4096
+    assert a < 4 * 4096 * 201088 / 8      # far below one fp32 slice of z
+    # generic path (fp32, or d % 64 != 0) needs no scratch
+    assert kd.kd_teacher_topk_workspace_size(64, 96, 5000, 100, 64, kd.KD_F32) == 256
+    assert kd.kd_teacher_topk_workspace_size(64, 72, 5000, 100, 64, kd.KD_BF16) == 256
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 512, 8192, 100, 64, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 99, 100, 64, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 8192, 0, 64, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),
+    ((256, 512, 8192, 100, 0, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),
+    ((256, 510, 8192, 100, 64, kd.KD_BF16), kd.KD_ERR_UNSUPPORTED),
+    ((256, 512, 8192, 257, 64, kd.KD_BF16), kd.KD_ERR_UNSUPPORTED),
+    ((256, 16392, 8192, 100, 64, kd.KD_BF16), kd.KD_ERR_UNSUPPORTED),
+    ((256, 512, 8192, 100, 64, 5), kd.KD_ERR_UNSUPPORTED),
+])
+def test_teacher_workspace_size_rejects(args, code):
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_teacher_topk_workspace_size(*args)
+    assert e.value.status == code
+
+
+def _tk_call(**kw):
+    lib = kd.load_library()
+    a = dict(H=1, W=1, dtype=kd.KD_BF16, T=256, d=512, V=8192, K=100,
+             chunk=64, idx=1, logit=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kd_teacher_topk(a["H"], a["W"], a["dtype"], a["T"], a["d"],
+                               a["V"], a["K"], a["chunk"], a["idx"],
+                               a["logit"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=None), kd.KD_ERR_INVALID_ARG),
+    (dict(W=None), kd.KD_ERR_INVALID_ARG),
+    (dict(idx=None), kd.KD_ERR_INVALID_ARG),
+    (dict(logit=None), kd.KD_ERR_INVALID_ARG),
+    (dict(K=9000), kd.KD_ERR_INVALID_ARG),
+    (dict(chunk=-1), kd.KD_ERR_INVALID_ARG),
+    (dict(d=20), kd.KD_ERR_UNSUPPORTED),
+    (dict(K=300), kd.KD_ERR_UNSUPPORTED),
+    (dict(dtype=2), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=None), kd.KD_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), kd.KD_ERR_WORKSPACE),
+    (dict(ws=512 + 8), kd.KD_ERR_WORKSPACE),
+])
+def test_teacher_topk_rejects_before_any_hip_call(kw, code):
+    assert _tk_call(**kw) == code

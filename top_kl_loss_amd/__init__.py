@@ -19,7 +19,8 @@ __all__ = [
     "KD_F32", "KD_BF16", "KD_FLAG_ACCUMULATE_DW", "KD_MAX_K", "LIB_PATH",
     "KdError", "load_library", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd", "kd_status_string", "kd_set_launch_log",
-    "EXPORTED_SYMBOLS", "KERNEL_NAMES",
+    "EXPORTED_SYMBOLS", "KERNEL_NAMES", "KD_TOPK_MAX_K", "KD_TOPK_MAX_D",
+    "kd_teacher_topk_workspace_size", "kd_teacher_topk",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
@@ -28,12 +29,16 @@ KD_F32, KD_BF16 = 0, 1
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP = range(5)
 KD_FLAG_ACCUMULATE_DW = 1
 KD_MAX_K = 1024
+KD_TOPK_MAX_K = 256
+KD_TOPK_MAX_D = 16384
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
-                    "kd_status_string", "kd_set_launch_log")
+                    "kd_status_string", "kd_set_launch_log",
+                    "kd_teacher_topk_workspace_size", "kd_teacher_topk")
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
                 "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
-                "scale_g", "transpose_w")
+                "scale_g", "transpose_w", "tk_sample", "tk_theta", "tk_filter",
+                "tk_select", "tk_stream")
 
 _lib = None
 
@@ -65,6 +70,15 @@ def load_library(path: str = LIB_PATH):
         c.c_uint32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
         c.c_void_p, c.c_size_t, c.c_void_p]
     lib.kd_topk_kl_fwd_bwd.restype = c.c_int
+    lib.kd_teacher_topk_workspace_size.argtypes = [
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_int,
+        c.POINTER(c.c_size_t)]
+    lib.kd_teacher_topk_workspace_size.restype = c.c_int
+    lib.kd_teacher_topk.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
+        c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_size_t,
+        c.c_void_p]
+    lib.kd_teacher_topk.restype = c.c_int
     lib.kd_status_string.argtypes = [c.c_int]
     lib.kd_status_string.restype = c.c_char_p
     lib.kd_set_launch_log.argtypes = [
@@ -177,3 +191,50 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
     if sync:
         hip.synchronize(stream)
     return loss, rl, dH, dW
+
+
+def kd_teacher_topk_workspace_size(T, d, V, K, chunk, dtype) -> int:
+    """Workspace bytes for kd_teacher_topk (see the C header)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_teacher_topk_workspace_size(
+        int(T), int(d), int(V), int(K), int(chunk), int(dtype),
+        ctypes.byref(out)))
+    return out.value
+
+
+def kd_teacher_topk(H, W, K, chunk=None, *, workspace=None, stream=None,
+                    sync=True):
+    """Teacher top-K cache on the GPU: for each row of z = H W^T, the K
+    largest logits (fp32) and their ids (int32), by logit descending and
+    equal logits by id ascending.  H [T,d] and W [V,d] are bf16 or fp32
+    CUDA tensors.  Returns (ids [T,K], logits [T,K]).  ``stream`` and
+    ``sync`` as for kd_topk_kl_fwd_bwd."""
+    import torch
+    lib = load_library()
+    T, d = H.shape
+    V = W.shape[0]
+    chunk = T if chunk is None else int(chunk)
+    dt = _dtype_code(H)
+    if W.dtype != H.dtype or W.shape[1] != d:
+        raise ValueError("W must be [V, d] with H's dtype")
+    dev = H.device
+    for t in (H, W):
+        if not t.is_cuda or t.device != dev or not t.is_contiguous():
+            raise ValueError("H and W must be contiguous tensors on one GPU")
+    ws_bytes = kd_teacher_topk_workspace_size(T, d, V, K, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    ids = torch.empty(T, int(K), dtype=torch.int32, device=dev)
+    vals = torch.empty(T, int(K), dtype=torch.float32, device=dev)
+    from . import hip
+    torch.cuda.synchronize(dev)
+    hip.set_device(dev.index if dev.index is not None else 0)
+    _check(lib.kd_teacher_topk(
+        H.data_ptr(), W.data_ptr(), dt, T, d, V, int(K), chunk,
+        ids.data_ptr(), vals.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), stream))
+    if sync:
+        hip.synchronize(stream)
+    return ids, vals

@@ -108,6 +108,54 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   return L;
 }
 
+// ---- teacher top-K cache builder
+int check_tk_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
+                   kd_dtype dtype) {
+  if (T < 1 || d < 1 || V < 1 || K < 1 || chunk < 1 || K > V)
+    return KD_ERR_INVALID_ARG;
+  if (dtype != KD_F32 && dtype != KD_BF16) return KD_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || K > KD_TOPK_MAX_K || d > KD_TOPK_MAX_D) return KD_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  if (T * d >= lim || V * d >= lim || T * K >= lim || V >= lim - kd::SEG)
+    return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+struct TkLayout {
+  int C, nseg, ns, sstride;
+  bool fast;
+  size_t o_zs, o_thv, o_thi, o_cnt, o_ovf, o_cand, total;
+};
+
+TkLayout make_tk_layout(int64_t T, int64_t d, int64_t V, int32_t chunk, kd_dtype dtype) {
+  TkLayout L{};
+  L.C = (int)(chunk < T ? chunk : T);
+  L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
+  L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, (int64_t)L.nseg * kd::SEG);
+  if (L.nseg <= kd::TK_NSAMPLE) {
+    L.ns = L.nseg;
+    L.sstride = 1;
+  } else {
+    L.ns = kd::TK_NSAMPLE;
+    L.sstride = L.nseg / kd::TK_NSAMPLE;
+  }
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t C = L.C;
+  if (L.fast) {
+    L.o_zs = take(sizeof(float) * C * (size_t)L.ns * kd::SEG);
+    L.o_thv = take(sizeof(float) * C);
+    L.o_thi = take(sizeof(int32_t) * C);
+    L.o_cnt = take(sizeof(int32_t) * C);
+    L.o_ovf = take(sizeof(int32_t) * C);
+    L.o_cand = take(sizeof(uint64_t) * C * (size_t)kd::TK_CAP);
+  } else {
+    take(1);  // the generic path needs no scratch; keep the size non-zero
+  }
+  L.total = o;
+  return L;
+}
+
 int hip_fail(hipError_t e) {
   snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error: %s", hipGetErrorString(e));
   return KD_ERR_HIP;
@@ -212,6 +260,69 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
     return kd::launch_final_loss(rl, (int)T, scal, loss, s);
   });
   if (e != hipSuccess) return hip_fail(e);
+  return KD_OK;
+}
+
+int kd_teacher_topk_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                                   int32_t chunk, kd_dtype dtype, size_t *bytes_out) {
+  if (!bytes_out) return KD_ERR_INVALID_ARG;
+  const int st = check_tk_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  *bytes_out = make_tk_layout(T, d, V, chunk, dtype).total;
+  return KD_OK;
+}
+
+int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
+                    int64_t d, int64_t V, int32_t K, int32_t chunk,
+                    int32_t *topk_idx, float *topk_logit, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit) return KD_ERR_INVALID_ARG;
+  const int st = check_tk_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  const TkLayout L = make_tk_layout(T, d, V, chunk, dtype);
+  if (!workspace || workspace_bytes < L.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  kd::TkArgs a{};
+  a.H = H;
+  a.W = W;
+  a.T = (int)T;
+  a.d = (int)d;
+  a.V = (int)V;
+  a.K = K;
+  a.nseg = L.nseg;
+  a.ns = L.ns;
+  a.sstride = L.sstride;
+  a.ldzs = L.ns * kd::SEG;
+  a.cap = kd::TK_CAP;
+  a.out_idx = topk_idx;
+  a.out_val = topk_logit;
+  if (L.fast) {
+    a.zs = reinterpret_cast<float *>(ws + L.o_zs);
+    a.th_v = reinterpret_cast<float *>(ws + L.o_thv);
+    a.th_i = reinterpret_cast<int32_t *>(ws + L.o_thi);
+    a.cnt = reinterpret_cast<int32_t *>(ws + L.o_cnt);
+    a.ovf = reinterpret_cast<int32_t *>(ws + L.o_ovf);
+    a.cand = reinterpret_cast<uint64_t *>(ws + L.o_cand);
+  }
+  a.all_rows = L.fast ? 0 : 1;
+  const bool bf16 = dtype == KD_BF16;
+  hipError_t e = hipSuccess;
+  for (int64_t c0 = 0; c0 < T; c0 += L.C) {
+    a.c0 = c0;
+    a.C = (int)(T - c0 < L.C ? T - c0 : L.C);
+    if (L.fast) {
+      if ((e = logged(KD_KERNEL_TK_SAMPLE, s, [&] { return kd::launch_tk_sample(a, s); })) ||
+          (e = logged(KD_KERNEL_TK_THETA, s, [&] { return kd::launch_tk_theta(a, s); })) ||
+          (e = logged(KD_KERNEL_TK_FILTER, s, [&] { return kd::launch_tk_filter(a, s); })) ||
+          (e = logged(KD_KERNEL_TK_SELECT, s, [&] { return kd::launch_tk_select(a, s); })))
+        return hip_fail(e);
+    }
+    e = logged(KD_KERNEL_TK_STREAM, s, [&] { return kd::launch_tk_stream(a, bf16, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return KD_OK;
 }
 

@@ -103,4 +103,43 @@ hipError_t launch_gemm_logits(const SliceArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_gemm_dh(const SliceArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_gemm_dw(const SliceArgs &a, bool bf16, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Teacher top-K cache builder (z = H W^T, per row the K largest entries).
+
+// Sampled vocabulary segments per row (evenly spaced, segment 0 included);
+// the K-th best entry among them bounds the row's K-th best from below.
+constexpr int TK_NSAMPLE = 32;
+// Candidate slots per row; a row with more candidates than this is
+// recomputed by the row-streaming kernel.
+constexpr int TK_CAP = 8192;
+// Merge buffer of the row-streaming kernel (entries, a power of two).
+constexpr int TK_STREAM_BUF = 2048;
+
+struct TkArgs {
+  const void *H;     // [T, d] element type (teacher hidden states)
+  const void *W;     // [V, d] element type (teacher LM head)
+  int64_t c0;        // first token of the slice
+  int C;             // rows in this slice
+  int T, d, V, K;
+  int nseg;          // ceil(V / SEG)
+  int ns, sstride;   // sampled segments: j * sstride for j < ns
+  float *zs;         // [Cmax, ns * SEG] logits of the sampled segments
+  int ldzs;          // ns * SEG
+  float *th_v;       // [Cmax] value of the row's threshold entry
+  int32_t *th_i;     // [Cmax] id of the row's threshold entry
+  int32_t *cnt;      // [Cmax] candidates appended
+  int32_t *ovf;      // [Cmax] 1 when the candidate slots overflowed
+  uint64_t *cand;    // [Cmax, cap] candidate keys
+  int cap;
+  int32_t *out_idx;  // [T, K]
+  float *out_val;    // [T, K]
+  int all_rows;      // row-streaming kernel: every row, not only overflows
+};
+
+hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s);
+hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s);
+hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s);
+hipError_t launch_tk_select(const TkArgs &a, hipStream_t s);
+hipError_t launch_tk_stream(const TkArgs &a, bool bf16, hipStream_t s);
+
 }  // namespace kd

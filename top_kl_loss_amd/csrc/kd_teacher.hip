@@ -1,0 +1,428 @@
+// Teacher top-K cache builder: for every token row t, the K largest entries
+// of z[t,:] = H[t,:] W^T (the teacher's LM-head logits) with their
+// vocabulary ids, sorted by value descending, equal values by id ascending.
+// This is the offline step of the method ("Making Knowledge Distillation
+// Cheap Enough to Run at Scale", aipuls.nl, section "Summary": the teacher
+// runs once and its top-100 logits per position are cached), built so that
+// the token-by-vocabulary logit matrix never exists.
+//
+// Order.  Every entry (value v, id i) is mapped to a 64-bit key whose high
+// word decreases as v increases (an order-preserving map of the fp32 bits,
+// -0 folded onto +0) and whose low word is i; a smaller key is a better
+// entry, and keys are distinct within a row.  The K best entries are the K
+// smallest keys.
+//
+// Tuned path (bf16, d % 64 == 0), per slice of C rows:
+//  1. k_tk_gemm<SAMPLE>: logits of TK_NSAMPLE evenly spaced vocabulary
+//     segments (segment 0 included), written to a small [C, ns*256] buffer.
+//  2. k_tk_theta: per row, the K-th smallest key among the sampled entries
+//     (radix select).  The K sampled entries are real entries of the row, so
+//     the row's K-th smallest key is no larger: every top-K entry has a key
+//     <= this threshold.  The K sampled entries at or below it are the first
+//     candidates of the row.
+//  3. k_tk_gemm<FILTER>: the logits of every other segment, on the same
+//     MFMA code as step 1; the epilogue appends the entries whose key is <=
+//     the row's threshold to the row's candidate list (about K * nseg / ns
+//     of them for logits without structure).
+//  4. k_tk_select: per row, the exact K smallest candidate keys (radix
+//     select, then a sort of those K).
+//  5. k_tk_stream: rows whose candidates overflowed TK_CAP slots are
+//     recomputed entry by entry and reduced with a streaming top-K.
+// Generic path (fp32 or d % 64 != 0): step 5 for every row.
+#include <stdint.h>
+
+#include "kd_device.h"
+#include "kd_internal.h"
+#include "kd_mfma_tile.h"
+
+namespace kd {
+
+namespace {
+
+using namespace tile;
+
+// ------------------------------------------------------------------ keys
+__device__ __forceinline__ uint32_t key_hi(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0u) u = 0u;  // -0 -> +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~ord;
+}
+__device__ __forceinline__ float key_val(uint32_t hi) {
+  const uint32_t ord = ~hi;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+__device__ __forceinline__ uint64_t make_key(float v, int id) {
+  return (uint64_t(key_hi(v)) << 32) | uint32_t(id);
+}
+
+// --------------------------------------------------- block-wide helpers
+// (256-thread workgroups)
+
+// Inclusive prefix sum of x over the workgroup in thread order; sc holds
+// at least 4 words.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t x, uint32_t *sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sc[wave] = x;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int w = 0; w < wave; ++w) off += sc[w];
+  return x + off;
+}
+
+// The r-th smallest (0-based) of n distinct 64-bit keys key_at(0..n-1), by
+// most-significant-byte-first radix selection: one 256-bin histogram per
+// byte over the keys that match the bytes chosen so far.  Needs r < n.
+// hist: 256 words, sc: 8 words, res: one key, all in LDS.
+template <class KeyAt>
+__device__ uint64_t block_select(KeyAt key_at, int n, int r, uint32_t *hist, uint32_t *sc,
+                                 uint64_t *res) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0, mask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t k = key_at(i);
+      if ((k & mask) == prefix) atomicAdd(&hist[uint32_t(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const uint32_t h = hist[tid];
+    const uint32_t incl = block_incl_scan(h, sc);
+    const uint32_t excl = incl - h;
+    if (excl <= uint32_t(r) && uint32_t(r) < incl) {
+      sc[4] = uint32_t(tid);
+      sc[5] = uint32_t(r) - excl;
+      sc[6] = h;
+    }
+    __syncthreads();
+    const uint32_t b = sc[4], hb = sc[6];
+    r = int(sc[5]);
+    prefix |= uint64_t(b) << shift;
+    mask |= uint64_t(0xffu) << shift;
+    __syncthreads();
+    if (hb == 1u && shift > 0) {
+      // one key left in the chosen bucket: it is the answer
+      for (int i = tid; i < n; i += 256) {
+        const uint64_t k = key_at(i);
+        if ((k & mask) == prefix) *res = k;
+      }
+      __syncthreads();
+      const uint64_t out = *res;
+      __syncthreads();
+      return out;
+    }
+  }
+  return prefix;
+}
+
+// Ascending bitonic sort of n (a power of two) keys in LDS.  The caller
+// synchronises before the call; the sorted keys are visible to all threads
+// on return.
+__device__ void bitonic_sort(uint64_t *s, int n) {
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
+        const int lo = ((t & ~(j - 1)) << 1) | (t & (j - 1)), hi = lo + j;
+        const bool up = (lo & k) == 0;
+        const uint64_t x = s[lo], y = s[hi];
+        if ((x > y) == up) {
+          s[lo] = y;
+          s[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Writes the first K keys of top[] (sorted) as the output row t.
+__device__ __forceinline__ void write_row(const TkArgs &a, int64_t t, const uint64_t *top) {
+  for (int k = threadIdx.x; k < a.K; k += blockDim.x) {
+    a.out_idx[t * a.K + k] = int32_t(uint32_t(top[k]));
+    a.out_val[t * a.K + k] = key_val(uint32_t(top[k] >> 32));
+  }
+}
+
+// ------------------------------------------------------------ the GEMM
+constexpr int SAMPLE = 0, FILTER = 1;
+
+// Tile (mt, segment) of z = H_c W^T on the tuned bf16 main loop.  SAMPLE:
+// the tile columns are sampled segment nt, stored to zs.  FILTER: every
+// non-sampled segment; entries with key <= the row's threshold are
+// appended to the row's candidates.
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void k_tk_gemm(TkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nmt = (a.C + BM - 1) / BM;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  int mt, nt;
+  group_tile(tile, nmt, MODE == SAMPLE ? a.ns : a.nseg, 4, mt, nt);
+  const int seg = MODE == SAMPLE ? nt * a.sstride : nt;
+  if (MODE == FILTER && seg % a.sstride == 0 && seg / a.sstride < a.ns) return;
+  const int m0 = mt * BM, n0 = seg * SEG;
+  const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
+  const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
+  CopyK<8> ca, cb;
+  ca.init(H, (uint64_t)a.C * a.d * 2, a.d, m0, wave, lane);
+  cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
+
+  // Epilogue layout (as the loss's logits GEMM): one block-row of every
+  // wave per pass, 64 rows x 256 columns, 8 threads per row.
+  constexpr int PITCH = BN + 4;
+  constexpr int SROWS = 64, TPR = NT / SROWS, CPT = BN / TPR;
+  const int sr = tid / TPR, part = tid % TPR;
+  float th_v[TM];
+  int th_i[TM];
+  if (MODE == FILTER) {
+    // thresholds of this thread's rows, fetched under the main loop
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
+      th_v[tm] = r < a.C ? a.th_v[r] : INFINITY;
+      th_i[tm] = r < a.C ? a.th_i[r] : -1;
+    }
+  }
+
+  f32x16 acc[TM][TN];
+  zero_acc(acc);
+  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  nt_loop(ca, cb, 0, a.d / BK, lds, ar, br, hh, acc);
+  __syncthreads();
+
+  float *stage = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        stage[(wm * 32 + acc_row(e, lane)) * PITCH + wn * WTN + tn * 32 + (lane & 31)] =
+            acc[tm][tn][e];
+    __syncthreads();
+    const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
+    const int cb0 = part * CPT;
+    const float *srow = stage + sr * PITCH + cb0;
+    if (MODE == SAMPLE) {
+      if (r < a.C) {
+        float *dst = a.zs + (size_t)r * a.ldzs + nt * SEG + cb0;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+          *reinterpret_cast<f32x4 *>(dst + c) = *reinterpret_cast<const f32x4 *>(srow + c);
+      }
+    } else {
+      const float tv = th_v[tm];
+      const int ti = th_i[tm];
+      uint32_t m = 0u;
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        const f32x4 z = *reinterpret_cast<const f32x4 *>(srow + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int id = n0 + cb0 + c + u;
+          const bool hit = z[u] > tv || (z[u] == tv && id <= ti);
+          m |= uint32_t(hit) << (c + u);
+        }
+      }
+      const int lim = a.V - (n0 + cb0);  // columns of this thread below V
+      if (lim < CPT) m = lim <= 0 ? 0u : (m & ((1u << lim) - 1u));
+      const int n = __popc(m);
+      int incl = n;
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        const int y = __shfl_up(incl, o, TPR);
+        if (part >= o) incl += y;
+      }
+      const int total = __shfl(incl, TPR - 1, TPR);
+      int base = 0;
+      if (part == TPR - 1 && total > 0 && r < a.C) base = atomicAdd(a.cnt + r, total);
+      base = __shfl(base, TPR - 1, TPR);
+      if (m != 0u && r < a.C) {
+        int pos = base + incl - n;
+        uint64_t *dst = a.cand + (size_t)r * a.cap;
+        while (m != 0u) {
+          const int i = __builtin_ctz(m);
+          m &= m - 1u;
+          if (pos < a.cap) dst[pos] = make_key(srow[i], n0 + cb0 + i);
+          ++pos;
+        }
+      }
+      if (part == TPR - 1 && r < a.C && total > 0 && base + total > a.cap) a.ovf[r] = 1;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- row threshold
+// One workgroup per row: the K-th smallest key among the sampled entries,
+// and those K entries as the row's first candidates.
+__global__ __launch_bounds__(256) void k_tk_theta(TkArgs a) {
+  __shared__ uint32_t hi[TK_NSAMPLE * SEG];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sc[8];
+  __shared__ uint64_t res;
+  __shared__ int nc;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int n = a.ns * SEG;
+  const int sstride = a.sstride;
+  const float *src = a.zs + (size_t)r * a.ldzs;
+  auto id_of = [sstride](int i) { return (i / SEG) * sstride * SEG + (i % SEG); };
+  for (int i = tid; i < n; i += 256) {
+    const int id = id_of(i);
+    // entries past the vocabulary rank after every real entry
+    hi[i] = id < a.V ? key_hi(src[i]) : 0xffffffffu;
+  }
+  if (tid == 0) nc = 0;
+  __syncthreads();
+  auto key_at = [&](int i) { return (uint64_t(hi[i]) << 32) | uint32_t(id_of(i)); };
+  const uint64_t th = block_select(key_at, n, a.K - 1, hist, sc, &res);
+  uint64_t *dst = a.cand + (size_t)r * a.cap;
+  for (int i = tid; i < n; i += 256) {
+    const uint64_t k = key_at(i);
+    if (k <= th) dst[atomicAdd(&nc, 1)] = k;
+  }
+  if (tid == 0) {
+    a.th_v[r] = key_val(uint32_t(th >> 32));
+    a.th_i[r] = int32_t(uint32_t(th));
+    a.cnt[r] = a.K;
+    a.ovf[r] = 0;
+  }
+}
+
+// ------------------------------------------------------- exact selection
+// One workgroup per row: the K smallest candidate keys, sorted.  Rows whose
+// candidates overflowed are left to k_tk_stream.
+__global__ __launch_bounds__(256) void k_tk_select(TkArgs a) {
+  extern __shared__ uint64_t keys[];  // TK_CAP
+  __shared__ uint64_t top[256];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sc[8];
+  __shared__ uint64_t res;
+  __shared__ int nsel;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (a.ovf[r]) return;
+  const int cnt = a.cnt[r];
+  const int n = cnt < a.cap ? cnt : a.cap;
+  const uint64_t *src = a.cand + (size_t)r * a.cap;
+  for (int i = tid; i < n; i += 256) keys[i] = src[i];
+  if (tid == 0) nsel = 0;
+  __syncthreads();
+  const uint64_t th = block_select([&](int i) { return keys[i]; }, n, a.K - 1, hist, sc, &res);
+  for (int i = tid; i < n; i += 256)
+    if (keys[i] <= th) top[atomicAdd(&nsel, 1)] = keys[i];
+  const int P = pow2_at_least(a.K);
+  for (int i = a.K + tid; i < P; i += 256) top[i] = ~0ull;
+  __syncthreads();
+  bitonic_sort(top, P);
+  write_row(a, a.c0 + r, top);
+}
+
+// ------------------------------------------------- row-streaming top-K
+// One workgroup per row: z[t, v] = sum_j H[t,j] W[v,j] in fp32 (fused
+// multiply-adds in j order), 256 ids at a time; entries better than the
+// current K-th are buffered and merged (sorted) when the buffer fills.
+template <typename T>
+__global__ __launch_bounds__(256) void k_tk_stream(TkArgs a) {
+  extern __shared__ float hs[];  // d
+  __shared__ uint64_t arr[TK_STREAM_BUF];
+  __shared__ int s_nbuf;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (!a.all_rows && !a.ovf[r]) return;
+  constexpr int E = Elem<T>::PER16B;
+  const int64_t t = a.c0 + r;
+  const T *Hr = reinterpret_cast<const T *>(a.H) + t * a.d;
+  for (int j = tid; j < a.d; j += 256) hs[j] = Elem<T>::to_f(Hr[j]);
+  if (tid == 0) s_nbuf = 0;
+  __syncthreads();
+  const T *W = reinterpret_cast<const T *>(a.W);
+  int nbest = 0;
+  uint64_t thr = ~0ull;
+  for (int base = 0; base < a.V; base += 256) {
+    const int v = base + tid;
+    if (v < a.V) {
+      const T *w = W + (size_t)v * a.d;
+      float acc = 0.f;
+      for (int j = 0; j < a.d; j += E) {
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(w + j);
+        if constexpr (E == 8) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            acc = fmaf(hs[j + 2 * p], bf16_lo(q[p]), acc);
+            acc = fmaf(hs[j + 2 * p + 1], bf16_hi(q[p]), acc);
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) acc = fmaf(hs[j + p], __uint_as_float(q[p]), acc);
+        }
+      }
+      const uint64_t key = make_key(acc, v);
+      if (key < thr) arr[nbest + atomicAdd(&s_nbuf, 1)] = key;
+    }
+    __syncthreads();
+    const int nbuf = s_nbuf;
+    __syncthreads();
+    if (nbest + nbuf + 256 > TK_STREAM_BUF || base + 256 >= a.V) {
+      const int n = nbest + nbuf;
+      const int P = pow2_at_least(n);
+      for (int i = n + tid; i < P; i += 256) arr[i] = ~0ull;
+      if (tid == 0) s_nbuf = 0;
+      __syncthreads();
+      bitonic_sort(arr, P);
+      nbest = n < a.K ? n : a.K;
+      thr = nbest == a.K ? arr[a.K - 1] : ~0ull;
+    }
+  }
+  write_row(a, t, arr);
+}
+
+template <typename K>
+hipError_t launch_dyn(K kern, int grid, int threads, int lds_bytes, const TkArgs &a, hipStream_t s) {
+  static_assert(sizeof(TkArgs) < 4096, "kernel argument size");
+  if (grid <= 0) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s) {
+  return launch_dyn(k_tk_gemm<SAMPLE>, ((a.C + BM - 1) / BM) * a.ns, NT, LDS_BYTES, a, s);
+}
+
+hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s) {
+  if (a.C <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tk_theta, dim3(a.C), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s) {
+  if (a.ns == a.nseg) return hipSuccess;  // every segment was sampled
+  return launch_dyn(k_tk_gemm<FILTER>, ((a.C + BM - 1) / BM) * a.nseg, NT, LDS_BYTES, a, s);
+}
+
+hipError_t launch_tk_select(const TkArgs &a, hipStream_t s) {
+  return launch_dyn(k_tk_select, a.C, 256, a.cap * (int)sizeof(uint64_t), a, s);
+}
+
+hipError_t launch_tk_stream(const TkArgs &a, bool bf16, hipStream_t s) {
+  const int lds = a.d * (int)sizeof(float);
+  return bf16 ? launch_dyn(k_tk_stream<uint16_t>, a.C, 256, lds, a, s)
+              : launch_dyn(k_tk_stream<float>, a.C, 256, lds, a, s);
+}
+
+}  // namespace kd
