@@ -36,27 +36,107 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+# Kernels whose HBM traffic bench.py reports, the symbol text that names them
+# in a rocprofv3 counter file, and the sources that determine their code.
+_GEMM_SRC = ("kd_gemm_fast.hip", "kd_mfma_tile.h", "kd_device.h", "kd_internal.h")
+_ROW_SRC = ("kd_rowops.hip", "kd_device.h", "kd_internal.h")
+_TK_SRC = ("kd_teacher.hip", "kd_mfma_tile.h", "kd_device.h", "kd_internal.h")
+TRAFFIC_KERNELS = {
+    "loss": [("k_fast_logits(", "gemm_logits", _GEMM_SRC),
+             ("k_fast_dh(", "gemm_dh", _GEMM_SRC),
+             ("k_fast_dw(", "gemm_dw", _GEMM_SRC),
+             ("k_scale_g(", "scale_g", _GEMM_SRC),
+             ("k_transpose_w(", "transpose_w", _GEMM_SRC),
+             ("k_transpose_h(", "transpose_h", _GEMM_SRC),
+             ("k_lse_fix<", "lse_fix", _ROW_SRC),
+             ("k_reduce_dh(", "reduce_dh", _ROW_SRC),
+             ("k_prep_rows(", "prep_rows", _ROW_SRC)],
+    "teacher_topk": [("k_tk_gemm<0>", "tk_sample", _TK_SRC),
+                     ("k_tk_gemm<1>", "tk_filter", _TK_SRC),
+                     ("k_tk_theta(", "tk_theta", _TK_SRC),
+                     ("k_tk_select(", "tk_select", _TK_SRC),
+                     ("k_tk_stream<", "tk_stream", _TK_SRC)],
+}
+
+
+def source_sha(files):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_kl_loss_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, launches_per_step):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when the kernel sources changed since they were taken."""
+def traffic_for(kernel, config_key):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs, or None when they were taken on another configuration or the
+    kernel's sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            k = json.load(f)["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
+        return None
+    if k.get("config") != config_key or k.get("source_sha") != source_sha(k["sources"]):
+        return None
+    return k.get("bytes_per_launch")
+
+
+def record_traffic(op, config_key, fetch_dir, write_dir, copy_bytes):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the op's kernels from two
+    rocprofv3 --pmc runs (csv output), scaled by what the same counter reads
+    for the runtime's device-to-device copy of copy_bytes (a reference of
+    known traffic), into profiles/traffic.json."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                              recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copy = [v for n, vs in vals.items() if "copyBuffer" in n for v in vs]
+        if not copy:
+            raise SystemExit(f"no copy-kernel dispatch in {d}: run with --copy-calibration")
+        factor = copy_bytes / (max(copy) * 1024.0)
+        for pat, name, srcs in TRAFFIC_KERNELS[op]:
+            vs = [v for n, v_ in vals.items() if pat in n for v in v_]
+            if not vs:
+                continue
+            k = out.setdefault(name, {"config": config_key, "sources": list(srcs),
+                                      "source_sha": source_sha(srcs),
+                                      "dispatches": len(vs)})
+            kib = sum(vs) / len(vs)
+            key = "fetch" if counter == "FETCH_SIZE" else "write"
+            k[f"{key}_kib_raw"] = round(kib)
+            k[f"{key}_factor"] = round(factor, 4)
+            k[f"{key}_bytes_per_launch"] = int(kib * 1024 * factor)
+    for k in out.values():
+        k["bytes_per_launch"] = k.get("fetch_bytes_per_launch", 0) + \
+            k.get("write_bytes_per_launch", 0)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("source_sha") != kernel_source_sha():
-        return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+        rec = {}
+    rec.setdefault("kernels", {})
+    rec["about"] = ("HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE and "
+                    "WRITE_SIZE runs (one counter per run), each scaled so that "
+                    "a device-to-device copy of known size reads and writes its "
+                    "own size; written by bench.py --record-traffic")
+    rec["kernels"].update(out)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    log(f"traffic of {sorted(out)} written to {TRAFFIC_FILE}")
 
 
 def cpu_baseline(x, target_s):
@@ -92,6 +172,14 @@ def cpu_baseline(x, target_s):
                       f"chunk; {dt:.1f} s wall"}
 
 
+def config_key(args):
+    """The configuration a traffic record belongs to."""
+    import synth
+    spec = synth.WORKLOADS[args.workload]
+    default = 4096 if args.op == "teacher_topk" else spec["chunk"]
+    return f"{args.op} {args.workload} chunk {args.chunk or default}"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +192,11 @@ def main():
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE; csv output) of this "
+                         "--op/--workload/--chunk made with --copy-calibration "
+                         "BYTES, then exit (no GPU needed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed region, copy BYTES device-to-device "
                          "3 times (a reference kernel of known traffic for "
@@ -116,6 +209,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.record_traffic:
+        if not args.copy_calibration:
+            raise SystemExit("--record-traffic needs --copy-calibration BYTES")
+        return record_traffic(args.op, config_key(args), *args.record_traffic,
+                              args.copy_calibration)
     if args.op == "teacher_topk":
         return bench_teacher(args)
 
@@ -246,7 +344,7 @@ def main():
         roof = {"bound": "mfma", "kernel": kd.KERNEL_NAMES[dom],
                 "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_for(kd.KERNEL_NAMES[dom], launches_per_step),
+                "traffic": traffic_for(kd.KERNEL_NAMES[dom], config_key(args)),
                 "launch_ms": round(dom_avg, 4), "launches": len(dom_ms),
                 "flops_per_launch": flops_launch}
     else:
@@ -421,7 +519,7 @@ def bench_teacher(args):
         roof = {"bound": "mfma", "kernel": TK_KINDS[dom], "achieved": round(ach, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_for(TK_KINDS[dom], None),
+                "traffic": traffic_for(TK_KINDS[dom], config_key(args)),
                 "launch_ms": round(dom_avg, 4), "launches": len(dom_ms),
                 "flops_per_launch": flops_launch}
     else:
