@@ -108,7 +108,7 @@ def record_traffic(op, config_key, fetch_dir, write_dir, copy_bytes):
         if not copy:
             raise SystemExit(f"no copy-kernel dispatch in {d}: run with --copy-calibration")
         factor = copy_bytes / (max(copy) * 1024.0)
-        for pat, name, srcs in TRAFFIC_KERNELS[op]:
+        for pat, name, srcs in TRAFFIC_KERNELS["teacher_topk" if op == "teacher_topk" else "loss"]:
             vs = [v for n, v_ in vals.items() if pat in n for v in v_]
             if not vs:
                 continue
@@ -185,8 +185,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--op", choices=("loss", "teacher_topk"), default="loss",
-                    help="loss: kd_topk_kl_fwd_bwd (default); teacher_topk: "
+    ap.add_argument("--op", choices=("loss", "fwd", "bwd", "teacher_topk"),
+                    default="loss",
+                    help="loss: kd_topk_kl_fwd_bwd (default); fwd: "
+                         "kd_topk_kl_fwd (loss only); bwd: kd_topk_kl_bwd "
+                         "(gradients, logits recomputed); teacher_topk: "
                          "kd_teacher_topk, the teacher cache build")
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
@@ -256,12 +259,27 @@ def main():
     hip.set_device(0)
     stream = hip.Stream()
 
+    mptr = None if mask is None else mask.data_ptr()
+    lse = torch.empty(T, **f32)
+    grad_loss = torch.ones(1, **f32)
+
     def step():
-        st = lib.kd_topk_kl_fwd_bwd(
-            H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
-            None if mask is None else mask.data_ptr(), T, d, V, K,
-            float(x.tau), chunk, 0, loss.data_ptr(), rl.data_ptr(),
-            dH.data_ptr(), dW.data_ptr(), ws.data_ptr(), ws_bytes, stream.value)
+        if args.op == "fwd":
+            st = lib.kd_topk_kl_fwd(
+                H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+                mptr, T, d, V, K, float(x.tau), chunk, loss.data_ptr(),
+                rl.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, stream.value)
+        elif args.op == "bwd":
+            st = lib.kd_topk_kl_bwd(
+                H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+                mptr, T, d, V, K, float(x.tau), chunk, 0, grad_loss.data_ptr(),
+                dH.data_ptr(), dW.data_ptr(), ws.data_ptr(), ws_bytes, stream.value)
+        else:
+            st = lib.kd_topk_kl_fwd_bwd(
+                H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+                mptr, T, d, V, K, float(x.tau), chunk, 0, loss.data_ptr(),
+                rl.data_ptr(), dH.data_ptr(), dW.data_ptr(), ws.data_ptr(),
+                ws_bytes, stream.value)
         if st != 0:
             raise RuntimeError(kd.kd_status_string(st))
 
@@ -335,7 +353,7 @@ def main():
     dom_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
     dom_avg = sum(dom_ms) / len(dom_ms)
 
-    flops_step = 6.0 * T * d * V
+    flops_step = (2.0 if args.op == "fwd" else 6.0) * T * d * V
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     tokens_s = T * args.steps / wall
     flops_launch = 2.0 * chunk * d * V if dom in GEMM_KERNELS else None
@@ -352,10 +370,13 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
                 "traffic": None, "launch_ms": round(dom_avg, 4)}
 
-    # sanity: the loss is finite
-    lval = float(loss.item())
+    lval = float(loss.item()) if args.op != "bwd" else None
+    metric = {"loss": METRIC,
+              "fwd": METRIC.replace("fwd+bwd", "forward only (kd_topk_kl_fwd)"),
+              "bwd": METRIC.replace("fwd+bwd", "backward with logits recomputed "
+                                    "(kd_topk_kl_bwd)")}[args.op]
     out = {
-        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s",
+        "metric": metric, "value": round(tokens_s, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": x.dtype,
@@ -372,7 +393,7 @@ def main():
         "kernel_ms_one_step": split,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "loss":
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

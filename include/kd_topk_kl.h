@@ -132,6 +132,53 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
                        float *loss, float *row_loss, float *dH, float *dW,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kd_topk_kl_fwd -- the loss alone (no gradients): the forward half of the
+ * loss for evaluation, or for training with kd_topk_kl_bwd when the
+ * backward runs later (the student training step of "Making Knowledge
+ * Distillation Cheap Enough to Run at Scale", aipuls.nl, section
+ * "Summary").  Arguments as for kd_topk_kl_fwd_bwd; in addition
+ *   lse   [T] fp32 output logsumexp_v z[t,v]/tau of every row (padding rows
+ *         too), or NULL.
+ * loss and row_loss are bitwise those of kd_topk_kl_fwd_bwd.  It runs the
+ * logits GEMM and the row reductions only: about a third of the work.  The
+ * workspace is sized by kd_topk_kl_workspace_size.
+ */
+int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
+                   const int32_t *topk_idx, const float *topk_logit,
+                   const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                   int32_t K, float tau, int32_t chunk, float *loss,
+                   float *row_loss, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * kd_topk_kl_bwd -- dH and dW of grad_loss * loss, recomputing the logits
+ * slice by slice (nothing is kept from kd_topk_kl_fwd).  Arguments as for
+ * kd_topk_kl_fwd_bwd; in addition
+ *   grad_loss  device pointer to one fp32: the upstream gradient of the
+ *              loss (NULL: 1).  It scales the logit gradient G before both
+ *              GEMMs, so dH and dW equal grad_loss times kd_topk_kl_fwd_bwd's
+ *              up to fp32 rounding.
+ * loss and row_loss are not produced.
+ */
+int kd_topk_kl_bwd(const void *H, const void *W, kd_dtype dtype,
+                   const int32_t *topk_idx, const float *topk_logit,
+                   const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                   int32_t K, float tau, int32_t chunk, uint32_t flags,
+                   const float *grad_loss, float *dH, float *dW,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kd_grad_cast -- dst[i] = src[i] * (*scale) for i < n, in dst_dtype (bf16
+ * rounded to nearest even): hands a gradient computed in fp32 back to a
+ * bf16 or fp32 parameter, scaled by a device-resident upstream gradient
+ * (scale NULL: 1).  src [n] fp32 and dst [n] are device memory and may be
+ * the same buffer when dst_dtype is KD_F32.  Returns KD_OK,
+ * KD_ERR_INVALID_ARG (NULL pointer, n < 0), KD_ERR_UNSUPPORTED or KD_ERR_HIP.
+ */
+int kd_grad_cast(const float *src, void *dst, kd_dtype dst_dtype, int64_t n,
+                 const float *scale, void *stream);
+
 /* Kernel ids for kd_set_launch_log (bit i of the mask selects id i). */
 enum {
   KD_KERNEL_VALID_COUNT = 0, /* N = sum(mask), gradient and loss scales     */
@@ -150,7 +197,8 @@ enum {
   KD_KERNEL_TK_THETA = 12,   /* per-row threshold from the sampled logits    */
   KD_KERNEL_TK_FILTER = 13,  /* logits of the other segments + candidates    */
   KD_KERNEL_TK_SELECT = 14,  /* exact top-K of each row's candidates         */
-  KD_KERNEL_TK_STREAM = 15   /* row-streaming top-K (generic path, overflow) */
+  KD_KERNEL_TK_STREAM = 15,  /* row-streaming top-K (generic path, overflow) */
+  KD_KERNEL_GRAD_CAST = 16   /* kd_grad_cast                                 */
 };
 
 /* Largest supported K and hidden size of kd_teacher_topk. */
@@ -215,7 +263,7 @@ int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
  * start_events/end_events hold hipEvent_t handles (as void*) created by the
  * caller in the same HIP runtime as this library; all arrays are host
  * memory owned by the caller and must outlive the calls they log.  The hook
- * applies to kd_topk_kl_fwd_bwd and kd_teacher_topk.  A zero
+ * applies to every entry point above.  A zero
  * `kernel_mask` (or NULL count) removes the hook.  Returns KD_OK, or
  * KD_ERR_INVALID_ARG for a non-zero mask with NULL events or capacity < 0.
  */

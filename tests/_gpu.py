@@ -68,3 +68,49 @@ def assert_loss_close(g, o, dtype):
     tol = TOL[dtype]["loss"]
     rel = abs(g - o) / max(abs(o), 1e-30)
     assert rel <= tol or (o == 0 and g == 0), f"loss {g} vs {o}: rel {rel:.3e}"
+
+
+# ------------------------------------------------------ teacher top-K cache
+# fp32 accumulation error of a logit, relative to sum_j |H[t,j] W[v,j]|
+# (about 2^-15.6: generous for d up to a few thousand, blocked or sequential)
+TOPK_REL_TOL = 2e-5
+
+
+def check_topk(x, ids, vals, K, exact=False, rows=None):
+    """Compare a teacher top-K cache (ids, vals: [len(rows), K]) with the
+    fp64 oracle on rows `rows` (default all) of the problem x: ids and
+    values exactly, or values within the fp32 rounding tolerance, the order,
+    and the id set wherever values closer than the tolerance do not decide."""
+    from oracle import teacher_topk as tko
+    rows = np.arange(x.H.shape[0]) if rows is None else np.asarray(rows)
+    Hs = x.H[rows]
+    o_ids, o_vals = tko.teacher_topk_cache(Hs, x.W, K)
+    if exact:
+        assert np.array_equal(ids, o_ids), "ids differ from the oracle"
+        assert np.array_equal(vals, o_vals), "logits differ from the oracle"
+        return
+    z = tko.teacher_logits(Hs, x.W)
+    absz = np.abs(Hs.astype(np.float64)) @ np.abs(x.W.astype(np.float64)).T
+    V = z.shape[1]
+    for t in range(len(rows)):
+        tol = TOPK_REL_TOL * absz[t].max() + 1e-30
+        row = ids[t]
+        where = f"row {int(rows[t])}"
+        assert len(set(row.tolist())) == K and row.min() >= 0 and row.max() < V
+        # values are the row's logits at the returned ids
+        assert np.abs(vals[t] - z[t, row]).max() <= tol, f"{where}: logit error"
+        # order: logit descending, equal logits by id ascending
+        dv = np.diff(vals[t])
+        assert np.all(dv <= 0), f"{where}: not sorted"
+        assert np.all(np.diff(row)[dv == 0] > 0), f"{where}: tie order"
+        # the sorted top-K logits agree with the oracle's
+        assert np.abs(vals[t] - o_vals[t]).max() <= 2 * tol, f"{where}: top-K values"
+        if K < V:
+            # no entry left out is better than an entry kept, beyond rounding
+            out = np.ones(V, dtype=bool)
+            out[row] = False
+            assert z[t, row].min() >= z[t, out].max() - 2 * tol, f"{where}: set"
+            # entries clearly inside the oracle's top-K are all returned
+            zk1 = np.sort(z[t])[::-1][K]
+            sure = o_ids[t][o_vals[t] > zk1 + 2 * tol]
+            assert set(sure.tolist()) <= set(row.tolist()), f"{where}: missing ids"

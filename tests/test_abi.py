@@ -167,3 +167,64 @@ def _tk_call(**kw):
 ])
 def test_teacher_topk_rejects_before_any_hip_call(kw, code):
     assert _tk_call(**kw) == code
+
+
+# ------------------------------------------ split forward / backward, cast
+def _fwd_call(**kw):
+    lib = kd.load_library()
+    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=1, row_loss=None,
+             lse=None, ws=256, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kd_topk_kl_fwd(
+        a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
+        a["d"], a["V"], a["K"], a["tau"], a["chunk"], a["loss"], a["row_loss"],
+        a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _bwd_call(**kw):
+    lib = kd.load_library()
+    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, g=None, dH=1,
+             dW=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kd_topk_kl_bwd(
+        a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
+        a["d"], a["V"], a["K"], a["tau"], a["chunk"], a["flags"], a["g"],
+        a["dH"], a["dW"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=None), kd.KD_ERR_INVALID_ARG),
+    (dict(loss=None), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=0.0), kd.KD_ERR_INVALID_ARG),
+    (dict(K=9000), kd.KD_ERR_INVALID_ARG),
+    (dict(d=12), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=None), kd.KD_ERR_WORKSPACE),
+    (dict(ws_bytes=100), kd.KD_ERR_WORKSPACE),
+])
+def test_fwd_rejects_before_any_hip_call(kw, code):
+    assert _fwd_call(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), kd.KD_ERR_INVALID_ARG),
+    (dict(dH=None), kd.KD_ERR_INVALID_ARG),
+    (dict(dW=None), kd.KD_ERR_INVALID_ARG),
+    (dict(flags=2), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), kd.KD_ERR_INVALID_ARG),
+    (dict(dtype=9), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=256 + 8), kd.KD_ERR_WORKSPACE),
+])
+def test_bwd_rejects_before_any_hip_call(kw, code):
+    assert _bwd_call(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 1, kd.KD_BF16, 4, None, None), kd.KD_ERR_INVALID_ARG),
+    ((1, None, kd.KD_BF16, 4, None, None), kd.KD_ERR_INVALID_ARG),
+    ((1, 1, kd.KD_BF16, -1, None, None), kd.KD_ERR_INVALID_ARG),
+    ((1, 1, 7, 4, None, None), kd.KD_ERR_UNSUPPORTED),
+])
+def test_grad_cast_rejects_before_any_hip_call(args, code):
+    assert kd.load_library().kd_grad_cast(*args) == code

@@ -137,3 +137,30 @@ def test_t32k_d4096_chunk_sweep():
                 assert err <= 2e-3, f"chunk {c}: {name} differs by {err:.2e}"
         del loss, rl, dH, dW
         torch.cuda.empty_cache()
+
+
+def test_teacher_topk_t32k_bench_configuration():
+    # the teacher cache build at the size bench.py --op teacher_topk times:
+    # T = 32768 rows of the t32k teacher head, K = 100, chunk 4096
+    import torch
+    import top_kl_loss_amd as kd
+    x = synth.teacher_head("t32k_teacher", case=3, T=32768, d=2880, V=201088)
+    _say("teacher top-K: T=32768 d=2880 V=201088 K=100 chunk=4096")
+    H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ids, vals = kd.kd_teacher_topk(H, W, 100, 4096)
+    ids = ids.cpu().numpy()
+    vals = vals.cpu().numpy().astype(np.float64)
+    # every row: ids in range and distinct, logits sorted (ties by id)
+    assert ids.min() >= 0 and ids.max() < x.V
+    srt = np.sort(ids, axis=1)
+    assert np.all(np.diff(srt, axis=1) > 0)
+    dv = np.diff(vals, axis=1)
+    assert np.all(dv <= 0) and np.all(np.diff(ids, axis=1)[dv == 0] > 0)
+    # sampled rows (first and last of slices, random) against the oracle
+    rng = np.random.default_rng(2024)
+    rows = sorted({0, 4095, 4096, 32767, *rng.choice(32768, 8, replace=False).tolist()})
+    _say(f"teacher top-K: oracle on rows {rows}")
+    G.check_topk(x, ids[rows], vals[rows], 100, rows=rows)
+    del H, W
+    torch.cuda.empty_cache()

@@ -20,7 +20,8 @@ __all__ = [
     "KdError", "load_library", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd", "kd_status_string", "kd_set_launch_log",
     "EXPORTED_SYMBOLS", "KERNEL_NAMES", "KD_TOPK_MAX_K", "KD_TOPK_MAX_D",
-    "kd_teacher_topk_workspace_size", "kd_teacher_topk",
+    "kd_teacher_topk_workspace_size", "kd_teacher_topk", "kd_topk_kl_fwd",
+    "kd_topk_kl_bwd", "kd_grad_cast",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
@@ -33,12 +34,13 @@ KD_TOPK_MAX_K = 256
 KD_TOPK_MAX_D = 16384
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log",
-                    "kd_teacher_topk_workspace_size", "kd_teacher_topk")
+                    "kd_teacher_topk_workspace_size", "kd_teacher_topk",
+                    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast")
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
                 "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
                 "scale_g", "transpose_w", "tk_sample", "tk_theta", "tk_filter",
-                "tk_select", "tk_stream")
+                "tk_select", "tk_stream", "grad_cast")
 
 _lib = None
 
@@ -79,6 +81,20 @@ def load_library(path: str = LIB_PATH):
         c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_size_t,
         c.c_void_p]
     lib.kd_teacher_topk.restype = c.c_int
+    lib.kd_topk_kl_fwd.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
+        c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    lib.kd_topk_kl_fwd.restype = c.c_int
+    lib.kd_topk_kl_bwd.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
+        c.c_uint32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_size_t, c.c_void_p]
+    lib.kd_topk_kl_bwd.restype = c.c_int
+    lib.kd_grad_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int64,
+                                 c.c_void_p, c.c_void_p]
+    lib.kd_grad_cast.restype = c.c_int
     lib.kd_status_string.argtypes = [c.c_int]
     lib.kd_status_string.restype = c.c_char_p
     lib.kd_set_launch_log.argtypes = [
@@ -126,24 +142,10 @@ def _dtype_code(t):
     raise TypeError(f"H/W must be bfloat16 or float32, got {t.dtype}")
 
 
-def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
-                       chunk=None, flags=0, *, dW=None, row_loss=True,
-                       workspace=None, stream=None, sync=True):
-    """Loss, per-row KL, dH and dW of the top-K KL loss on the GPU.
-
-    H [T,d] and W [V,d] (bf16 or fp32), topk_idx [T,K] int32, topk_logit
-    [T,K] fp32 and mask [T] (uint8/bool or None) are CUDA tensors.  Outputs
-    are allocated here (``dW`` may be passed in, e.g. with
-    KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW).
-
-    ``stream`` is a stream handle of the library's HIP runtime
-    (``top_kl_loss_amd.hip.Stream().value``) or None for its null stream.
-    With ``sync=False`` the call returns as soon as the work is enqueued;
-    the caller must then keep every tensor alive and synchronise the stream
-    (``top_kl_loss_amd.hip.synchronize``) before torch touches the results.
-    """
+def _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk):
+    """Validates the loss inputs; returns (T, d, V, K, chunk, dtype code,
+    mask as uint8 or None)."""
     import torch
-    lib = load_library()
     T, d = H.shape
     V = W.shape[0]
     K = topk_idx.shape[1]
@@ -166,11 +168,54 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
     for t in tensors:
         if not t.is_cuda or t.device != dev or not t.is_contiguous():
             raise ValueError("all inputs must be contiguous tensors on one GPU")
+    return T, d, V, K, chunk, dt, mask
+
+
+def _workspace(T, d, V, K, chunk, dt, workspace, dev):
+    import torch
     ws_bytes = kd_topk_kl_workspace_size(T, d, V, K, chunk, dt)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     elif workspace.numel() < ws_bytes:
         raise ValueError("workspace too small")
+    return workspace
+
+
+def _enter(dev):
+    """Orders the library's work after torch's pending work."""
+    import torch
+    from . import hip
+    torch.cuda.synchronize(dev)          # inputs written by torch are ready
+    hip.set_device(dev.index if dev.index is not None else 0)
+
+
+def _leave(stream, sync):
+    if sync:
+        from . import hip
+        hip.synchronize(stream)
+
+
+def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                       chunk=None, flags=0, *, dW=None, row_loss=True,
+                       workspace=None, stream=None, sync=True):
+    """Loss, per-row KL, dH and dW of the top-K KL loss on the GPU.
+
+    H [T,d] and W [V,d] (bf16 or fp32), topk_idx [T,K] int32, topk_logit
+    [T,K] fp32 and mask [T] (uint8/bool or None) are CUDA tensors.  Outputs
+    are allocated here (``dW`` may be passed in, e.g. with
+    KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW).
+
+    ``stream`` is a stream handle of the library's HIP runtime
+    (``top_kl_loss_amd.hip.Stream().value``) or None for its null stream.
+    With ``sync=False`` the call returns as soon as the work is enqueued;
+    the caller must then keep every tensor alive and synchronise the stream
+    (``top_kl_loss_amd.hip.synchronize``) before torch touches the results.
+    """
+    import torch
+    lib = load_library()
+    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    dev = H.device
+    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     loss = torch.empty(1, **f32)
     rl = torch.empty(T, **f32) if row_loss else None
@@ -179,18 +224,99 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
         dW = torch.empty(V, d, **f32)
     elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
         raise ValueError("dW must be float32 [V, d]")
-    from . import hip
-    torch.cuda.synchronize(dev)          # inputs written by torch are ready
-    hip.set_device(dev.index if dev.index is not None else 0)
+    _enter(dev)
     _check(lib.kd_topk_kl_fwd_bwd(
         H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
         topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
         T, d, V, K, float(tau), chunk, int(flags), loss.data_ptr(),
         rl.data_ptr() if rl is not None else None, dH.data_ptr(),
         dW.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
-    if sync:
-        hip.synchronize(stream)
+    _leave(stream, sync)
     return loss, rl, dH, dW
+
+
+def kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                   chunk=None, *, row_loss=True, lse=True, workspace=None,
+                   stream=None, sync=True):
+    """The loss alone.  Returns (loss[1], row_loss[T] or None, lse[T] or
+    None); arguments as for kd_topk_kl_fwd_bwd."""
+    import torch
+    lib = load_library()
+    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    dev = H.device
+    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    rl = torch.empty(T, **f32) if row_loss else None
+    ls = torch.empty(T, **f32) if lse else None
+    _enter(dev)
+    _check(lib.kd_topk_kl_fwd(
+        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
+        T, d, V, K, float(tau), chunk, loss.data_ptr(),
+        rl.data_ptr() if rl is not None else None,
+        ls.data_ptr() if ls is not None else None,
+        workspace.data_ptr(), workspace.numel(), stream))
+    _leave(stream, sync)
+    return loss, rl, ls
+
+
+def kd_topk_kl_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                   chunk=None, flags=0, grad_loss=None, *, dW=None,
+                   workspace=None, stream=None, sync=True):
+    """dH and dW (fp32) of grad_loss * loss.  ``grad_loss`` is None (1) or a
+    one-element fp32 CUDA tensor.  Returns (dH, dW)."""
+    import torch
+    lib = load_library()
+    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    dev = H.device
+    if grad_loss is not None:
+        if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1
+                or grad_loss.device != dev):
+            raise ValueError("grad_loss must be one float32 value on H's device")
+        grad_loss = grad_loss.contiguous()
+    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dH = torch.empty(T, d, **f32)
+    if dW is None:
+        dW = torch.empty(V, d, **f32)
+    elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
+        raise ValueError("dW must be float32 [V, d]")
+    _enter(dev)
+    _check(lib.kd_topk_kl_bwd(
+        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
+        T, d, V, K, float(tau), chunk, int(flags),
+        grad_loss.data_ptr() if grad_loss is not None else None,
+        dH.data_ptr(), dW.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        stream))
+    _leave(stream, sync)
+    return dH, dW
+
+
+def kd_grad_cast(src, dtype, scale=None, *, out=None, stream=None, sync=True):
+    """src (fp32 CUDA tensor) times scale (None or a one-element fp32 CUDA
+    tensor) as a new tensor of torch dtype ``dtype`` (bfloat16 or float32),
+    or into ``out``."""
+    import torch
+    lib = load_library()
+    if src.dtype != torch.float32 or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous float32 CUDA tensor")
+    code = KD_BF16 if dtype == torch.bfloat16 else KD_F32 if dtype == torch.float32 else None
+    if code is None:
+        raise TypeError(f"unsupported dtype {dtype}")
+    if out is None:
+        out = torch.empty(src.shape, dtype=dtype, device=src.device)
+    elif out.dtype != dtype or out.shape != src.shape or not out.is_contiguous():
+        raise ValueError("out must match src's shape and the dtype")
+    if scale is not None and (scale.dtype != torch.float32 or scale.numel() != 1):
+        raise ValueError("scale must be one float32 value")
+    _enter(src.device)
+    _check(lib.kd_grad_cast(src.data_ptr(), out.data_ptr(), code, src.numel(),
+                            scale.data_ptr() if scale is not None else None,
+                            stream))
+    _leave(stream, sync)
+    return out
 
 
 def kd_teacher_topk_workspace_size(T, d, V, K, chunk, dtype) -> int:

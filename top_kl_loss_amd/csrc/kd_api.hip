@@ -174,14 +174,21 @@ int kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
   return KD_OK;
 }
 
-int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
-                       const int32_t *topk_idx, const float *topk_logit,
-                       const uint8_t *mask, int64_t T, int64_t d, int64_t V,
-                       int32_t K, float tau, int32_t chunk, uint32_t flags,
-                       float *loss, float *row_loss, float *dH, float *dW,
-                       void *workspace, size_t workspace_bytes, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW)
-    return KD_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+enum LossMode { MODE_FWD_BWD, MODE_FWD, MODE_BWD };
+
+// The slice loop of the three loss entry points.  MODE_FWD skips the
+// probability store, G and both backward GEMMs; MODE_BWD skips the loss sum
+// and scales G by *grad_loss.
+int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
+             const int32_t *topk_idx, const float *topk_logit, const uint8_t *mask,
+             int64_t T, int64_t d, int64_t V, int32_t K, float tau, int32_t chunk,
+             uint32_t flags, const float *grad_loss, float *loss, float *row_loss,
+             float *lse_out, float *dH, float *dW, void *workspace,
+             size_t workspace_bytes, void *stream) {
   if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
   if (flags & ~uint32_t(KD_FLAG_ACCUMULATE_DW)) return KD_ERR_INVALID_ARG;
   const int st = check_sizes(T, d, V, K, chunk, dtype);
@@ -191,6 +198,7 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
       (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return KD_ERR_WORKSPACE;
 
+  const bool grads = mode != MODE_FWD;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   const bool bf16 = dtype == KD_BF16;
@@ -225,7 +233,7 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
   a.Ht = reinterpret_cast<uint16_t *>(ws + L.o_ht);
   a.Gt = reinterpret_cast<uint16_t *>(ws + L.o_gt);
-  a.Wt = L.wt ? reinterpret_cast<uint16_t *>(ws + L.o_wt) : nullptr;
+  a.Wt = (L.wt && grads) ? reinterpret_cast<uint16_t *>(ws + L.o_wt) : nullptr;
   a.ldh = L.ldh;
   a.dh_stride = (size_t)L.C * (size_t)d;
   a.splits = L.splits;
@@ -233,9 +241,12 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
   a.dH = dH;
   a.dW = dW;
   a.fast = L.fast ? 1 : 0;
+  a.need_grad = grads ? 1 : 0;
+  a.lse_out = lse_out;
 
   hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {
-    return kd::launch_valid_count(mask, (int)T, tau, scal, s);
+    return kd::launch_valid_count(mask, (int)T, tau, mode == MODE_BWD ? grad_loss : nullptr,
+                                  scal, s);
   });
   if (e != hipSuccess) return hip_fail(e);
   if (a.Wt) {
@@ -248,19 +259,75 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
     a.dw_beta = (c0 > 0 || (flags & KD_FLAG_ACCUMULATE_DW)) ? 1 : 0;
     if ((e = logged(KD_KERNEL_PREP_ROWS, s, [&] { return kd::launch_prep_rows(a, s); })) ||
         (e = logged(KD_KERNEL_GEMM_LOGITS, s, [&] { return kd::launch_gemm_logits(a, bf16, s); })) ||
-        (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })) ||
-        (a.fast && (e = logged(KD_KERNEL_SCALE_G, s, [&] { return kd::launch_scale_g(a, s); }))) ||
+        (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })))
+      return hip_fail(e);
+    if (!grads) continue;
+    if ((a.fast && (e = logged(KD_KERNEL_SCALE_G, s, [&] { return kd::launch_scale_g(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
         (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DW, s, [&] { return kd::launch_gemm_dw(a, bf16, s); })))
       return hip_fail(e);
   }
-  e = logged(KD_KERNEL_FINAL_LOSS, s, [&] {
-    return kd::launch_final_loss(rl, (int)T, scal, loss, s);
-  });
-  if (e != hipSuccess) return hip_fail(e);
+  if (mode != MODE_BWD) {
+    e = logged(KD_KERNEL_FINAL_LOSS, s, [&] {
+      return kd::launch_final_loss(rl, (int)T, scal, loss, s);
+    });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
+                       const int32_t *topk_idx, const float *topk_logit,
+                       const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                       int32_t K, float tau, int32_t chunk, uint32_t flags,
+                       float *loss, float *row_loss, float *dH, float *dW,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW)
+    return KD_ERR_INVALID_ARG;
+  return run_loss(MODE_FWD_BWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
+                  tau, chunk, flags, nullptr, loss, row_loss, nullptr, dH, dW,
+                  workspace, workspace_bytes, stream);
+}
+
+int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
+                   const int32_t *topk_idx, const float *topk_logit,
+                   const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                   int32_t K, float tau, int32_t chunk, float *loss,
+                   float *row_loss, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit || !loss) return KD_ERR_INVALID_ARG;
+  return run_loss(MODE_FWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
+                  tau, chunk, 0u, nullptr, loss, row_loss, lse, nullptr, nullptr,
+                  workspace, workspace_bytes, stream);
+}
+
+int kd_topk_kl_bwd(const void *H, const void *W, kd_dtype dtype,
+                   const int32_t *topk_idx, const float *topk_logit,
+                   const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                   int32_t K, float tau, int32_t chunk, uint32_t flags,
+                   const float *grad_loss, float *dH, float *dW, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit || !dH || !dW) return KD_ERR_INVALID_ARG;
+  return run_loss(MODE_BWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
+                  tau, chunk, flags, grad_loss, nullptr, nullptr, nullptr, dH, dW,
+                  workspace, workspace_bytes, stream);
+}
+
+int kd_grad_cast(const float *src, void *dst, kd_dtype dst_dtype, int64_t n,
+                 const float *scale, void *stream) {
+  if (!src || !dst || n < 0) return KD_ERR_INVALID_ARG;
+  if (dst_dtype != KD_F32 && dst_dtype != KD_BF16) return KD_ERR_UNSUPPORTED;
+  hipError_t e = logged(KD_KERNEL_GRAD_CAST, reinterpret_cast<hipStream_t>(stream), [&] {
+    return kd::launch_grad_cast(src, dst, dst_dtype == KD_BF16, n, scale,
+                                reinterpret_cast<hipStream_t>(stream));
+  });
+  return e == hipSuccess ? KD_OK : hip_fail(e);
 }
 
 int kd_teacher_topk_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,

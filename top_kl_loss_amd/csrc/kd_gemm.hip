@@ -320,7 +320,9 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_logits(SliceArgs a) {
     for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
     if (r < a.C) {
       T *dst = P + (size_t)r * a.ldp + n0 + c0;
-      if constexpr (sizeof(T) == 2) {
+      if (!a.need_grad) {
+        // forward only: the probabilities are not needed
+      } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int c = 0; c < CPT; c += 8) {
           u32x4 w{pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]),

@@ -117,11 +117,13 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
     if (r < a.C) {
       uint16_t *dst = P + (size_t)r * a.ldp + n0 + cb0;
+      if (a.need_grad) {
 #pragma unroll
-      for (int c = 0; c < CPT; c += 8) {
-        u32x4 w{pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]),
-                pack_bf16x2(v[c + 4], v[c + 5]), pack_bf16x2(v[c + 6], v[c + 7])};
-        *reinterpret_cast<u32x4 *>(dst + c) = w;
+        for (int c = 0; c < CPT; c += 8) {
+          u32x4 w{pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]),
+                  pack_bf16x2(v[c + 4], v[c + 5]), pack_bf16x2(v[c + 6], v[c + 7])};
+          *reinterpret_cast<u32x4 *>(dst + c) = w;
+        }
       }
       if (part == 0) {
         a.mseg[(size_t)r * a.nseg + seg] = mx;

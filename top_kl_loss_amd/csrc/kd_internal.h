@@ -67,6 +67,8 @@ struct SliceArgs {
   float *dW;         // [V, d]
   int dw_beta;       // 0: dW = G^T H, 1: dW += G^T H
   int fast;          // use the tuned bf16 kernels
+  int need_grad;     // 0: forward only (no P store, no G)
+  float *lse_out;    // [T] row logsumexp of z/tau, or null
 };
 
 // Tile shapes of the three GEMMs (all use 256-thread workgroups).
@@ -93,7 +95,9 @@ hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s);
 
 // Launch wrappers; each returns hipSuccess or the launch error.
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,
-                              Scalars *scal, hipStream_t s);
+                              const float *grad_loss, Scalars *scal, hipStream_t s);
+hipError_t launch_grad_cast(const float *src, void *dst, bool bf16, int64_t n,
+                            const float *scale, hipStream_t s);
 hipError_t launch_prep_rows(const SliceArgs &a, hipStream_t s);
 hipError_t launch_lse_fix(const SliceArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_reduce_dh(const SliceArgs &a, hipStream_t s);

@@ -23,8 +23,11 @@ constexpr int ROWS_PER_WG = 4;  // one wave per row
 // N = sum(mask), grad scale tau/N and loss scale tau^2/N (zero for N = 0).
 // Reading of the reduction: mean over valid tokens, as in the asibiont.com
 // article's implementation sketch, with tau^2 scaling of the soft loss.
+// grad_loss (device scalar, or null for 1) multiplies the grad scale: the
+// upstream gradient of the loss in a backward pass.
 __global__ __launch_bounds__(256) void k_valid_count(const uint8_t *mask, int T,
-                                                     float tau, Scalars *scal) {
+                                                     float tau, const float *grad_loss,
+                                                     Scalars *scal) {
   __shared__ int part[4];
   int cnt = 0;
   if (mask) {
@@ -39,7 +42,8 @@ __global__ __launch_bounds__(256) void k_valid_count(const uint8_t *mask, int T,
   if (threadIdx.x == 0) {
     const int n = part[0] + part[1] + part[2] + part[3];
     scal->n_valid = n;
-    scal->grad_scale = n > 0 ? float(double(tau) / double(n)) : 0.f;
+    const double g = grad_loss ? double(*grad_loss) : 1.0;
+    scal->grad_scale = n > 0 ? float(double(tau) / double(n) * g) : 0.f;
     scal->loss_scale = n > 0 ? float(double(tau) * tau / double(n)) : 0.f;
   }
 }
@@ -142,8 +146,10 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   const bool valid = a.mask ? (a.mask[t] != 0) : true;
   if (lane == 0) {
     a.lse[r] = lse;
+    if (a.lse_out) a.lse_out[t] = lse;
     a.row_loss[t] = valid ? (a.cterm[r] + lse - dot * a.inv_tau) : 0.f;
   }
+  if (!a.need_grad) return;
 
   const float gscale = valid ? a.scal->grad_scale : 0.f;
   T *P = reinterpret_cast<T *>(a.P) + (size_t)r * a.ldp;
@@ -204,6 +210,18 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   }
 }
 
+// dst[i] = src[i] * (*scale) (scale null: 1) in the destination type (bf16
+// rounded to nearest even): the gradient handed back to a bf16 or fp32
+// parameter.
+template <typename T>
+__global__ __launch_bounds__(256) void k_grad_cast(const float *src, T *dst, int64_t n,
+                                                   const float *scale) {
+  const float s = scale ? *scale : 1.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    dst[i] = Elem<T>::from_f(src[i] * s);
+}
+
 // dH rows of the slice = ordered sum of the split-K partials.
 __global__ __launch_bounds__(256) void k_reduce_dh(const float *part, int splits,
                                                    size_t stride, size_t n4,
@@ -238,8 +256,22 @@ __global__ __launch_bounds__(256) void k_final_loss(const float *row_loss, int T
 }  // namespace
 
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,
-                              Scalars *scal, hipStream_t s) {
-  hipLaunchKernelGGL(k_valid_count, dim3(1), dim3(256), 0, s, mask, T, tau, scal);
+                              const float *grad_loss, Scalars *scal, hipStream_t s) {
+  hipLaunchKernelGGL(k_valid_count, dim3(1), dim3(256), 0, s, mask, T, tau, grad_loss, scal);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_cast(const float *src, void *dst, bool bf16, int64_t n,
+                            const float *scale, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int g = (int)(want < 8192 ? want : 8192);
+  if (bf16)
+    hipLaunchKernelGGL(k_grad_cast<uint16_t>, dim3(g), dim3(256), 0, s, src,
+                       static_cast<uint16_t *>(dst), n, scale);
+  else
+    hipLaunchKernelGGL(k_grad_cast<float>, dim3(g), dim3(256), 0, s, src,
+                       static_cast<float *>(dst), n, scale);
   return hipGetLastError();
 }
 
