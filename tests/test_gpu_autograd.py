@@ -60,9 +60,12 @@ def test_backward_alone_scales_by_the_upstream_gradient(x, g):
         assert float(dH.abs().max()) == 0.0 and float(dW.abs().max()) == 0.0
         return
     _, _, fH, fW = G.run(dev, x.tau, x.chunk)
+    # fp32: G is scaled before one fp32 rounding; bf16: G is stored in bf16
+    # after the scaling, so the two differ by bf16 rounding of G
+    tol = 1e-5 if x.dtype == "f32" else G.TOL["bf16"]["maxrel"]
     for name, a, b in (("dH", dH, fH), ("dW", dW, fW)):
         err = float((a - g * b).abs().max()) / (g * float(b.abs().max()))
-        assert err <= 1e-5, f"{name}: {err:.2e} from {g} x fused"
+        assert err <= tol, f"{name}: {err:.2e} from {g} x fused"
     ref = orc.kd_topk_kl(x.H, x.W, x.topk_idx, x.topk_logit, x.mask, x.tau)
     G.assert_grad_close(G.to_np(dH), g * ref["dH"], x.dtype, "dH")
     G.assert_grad_close(G.to_np(dW), g * ref["dW"], x.dtype, "dW")
