@@ -40,7 +40,8 @@ def log(msg):
 # in a rocprofv3 counter file, and the sources that determine their code.
 _GEMM_SRC = ("kd_gemm_fast.hip", "kd_mfma_tile.h", "kd_device.h", "kd_internal.h")
 _ROW_SRC = ("kd_rowops.hip", "kd_device.h", "kd_internal.h")
-_TK_SRC = ("kd_teacher.hip", "kd_mfma_tile.h", "kd_device.h", "kd_internal.h")
+_TK_SRC = ("kd_teacher.hip", "kd_mfma_tile.h", "kd_select.h", "kd_device.h",
+           "kd_internal.h")
 TRAFFIC_KERNELS = {
     "loss": [("k_fast_logits(", "gemm_logits", _GEMM_SRC),
              ("k_fast_dh(", "gemm_dh", _GEMM_SRC),
@@ -185,12 +186,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--op", choices=("loss", "fwd", "bwd", "teacher_topk"),
+    ap.add_argument("--op", choices=("loss", "fwd", "bwd", "teacher_topk",
+                                     "entropy_filter"),
                     default="loss",
                     help="loss: kd_topk_kl_fwd_bwd (default); fwd: "
                          "kd_topk_kl_fwd (loss only); bwd: kd_topk_kl_bwd "
                          "(gradients, logits recomputed); teacher_topk: "
-                         "kd_teacher_topk, the teacher cache build")
+                         "kd_teacher_topk, the teacher cache build; "
+                         "entropy_filter: kd_entropy_filter (top 70% of "
+                         "tokens by teacher entropy)")
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -219,6 +223,8 @@ def main():
                               args.copy_calibration)
     if args.op == "teacher_topk":
         return bench_teacher(args)
+    if args.op == "entropy_filter":
+        return bench_filter(args)
 
     import numpy as np
     import torch
@@ -568,6 +574,78 @@ def bench_teacher(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_teacher(x, K, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_filter(args):
+    """One step = one kd_entropy_filter call (top-fraction mode, 70%) over
+    the workload's teacher cache: T rows of K fp32 logits."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+
+    torch.cuda.init()
+    lib = kd.load_library()
+    x = synth.workload(args.workload, teacher_device="cuda")
+    T, K = x.T, x.K
+    dev = torch.device("cuda:0")
+    lg = torch.from_numpy(x.topk_logit).to(dev)
+    mask = None if x.mask is None else torch.from_numpy(x.mask).to(dev)
+    ws_bytes = kd.kd_entropy_filter_workspace_size(T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(T, dtype=torch.uint8, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    hip.set_device(0)
+    stream = hip.Stream()
+
+    def step():
+        st = lib.kd_entropy_filter(lg.data_ptr(),
+                                   None if mask is None else mask.data_ptr(),
+                                   T, K, float(x.tau), 1, 0.7, out.data_ptr(),
+                                   ent.data_ptr(), ws.data_ptr(), ws_bytes,
+                                   stream.value)
+        if st != 0:
+            raise RuntimeError(kd.kd_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+    starts = [hip.Event() for _ in range(args.steps)]
+    ends = [hip.Event() for _ in range(args.steps)]
+    arr_s = (ctypes.c_void_p * args.steps)(*[e.value for e in starts])
+    arr_e = (ctypes.c_void_p * args.steps)(*[e.value for e in ends])
+    count = ctypes.c_int32(0)
+    kd.kd_set_launch_log(1 << 17, arr_s, arr_e, None, args.steps, ctypes.byref(count))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stream.synchronize()
+    wall = time.perf_counter() - t0
+    kd.kd_set_launch_log(0, None, None, None, 0, None)
+    call_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
+    avg = sum(call_ms) / len(call_ms)
+    # algorithmic bytes: read the logits and the mask, write entropy and mask
+    nbytes = T * K * 4 + 2 * T + 4 * T
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    kept = int(out.sum().item())
+    print(json.dumps({
+        "metric": "tokens/s entropy token filter (top 70% by teacher entropy) "
+                  "over the top-100 cache",
+        "value": round(T * args.steps / wall, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": x.name, "T": T, "K": K, "tau": x.tau,
+                   "mode": "top_fraction", "fraction": 0.7, "kept": kept},
+        "roofline": {"bound": "hbm", "kernel": "entropy_filter (3 launches)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+                     "traffic": None, "launch_ms": round(avg, 4)},
+    }), flush=True)
 
 
 if __name__ == "__main__":

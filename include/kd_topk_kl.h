@@ -179,6 +179,50 @@ int kd_topk_kl_bwd(const void *H, const void *W, kd_dtype dtype,
 int kd_grad_cast(const float *src, void *dst, kd_dtype dst_dtype, int64_t n,
                  const float *scale, void *stream);
 
+/* Modes of kd_entropy_filter. */
+enum {
+  KD_FILTER_ENTROPY_ABOVE = 0,       /* keep tokens with entropy > param   */
+  KD_FILTER_TOP_ENTROPY_FRACTION = 1 /* keep the fraction param of valid
+                                        tokens with the highest entropy    */
+};
+
+/* Bytes of device scratch kd_entropy_filter needs for T tokens (host
+ * pointer bytes_out).  Returns KD_OK, KD_ERR_INVALID_ARG or
+ * KD_ERR_UNSUPPORTED (T >= 2^31). */
+int kd_entropy_filter_workspace_size(int64_t T, size_t *bytes_out);
+
+/*
+ * kd_entropy_filter -- distillation token filtering by teacher entropy
+ * (asibiont.com article, sections "Distillation Token Filtering" and "A
+ * Concrete Implementation Sketch": tokens whose teacher distribution is
+ * nearly one-hot are skipped, by an entropy threshold or by keeping a fixed
+ * fraction of the batch's tokens with the highest entropy).  The teacher
+ * distribution is the loss's: q[t,:] = softmax(topk_logit[t,:] / tau) over
+ * the K cached logits, and entropy[t] = -sum_k q[t,k] log q[t,k] (no
+ * epsilon inside the log; q > 0).  Writes a token mask for the loss entry
+ * points:
+ *   KD_FILTER_ENTROPY_ABOVE         mask_out[t] = mask[t] && entropy[t] > param
+ *   KD_FILTER_TOP_ENTROPY_FRACTION  with N = sum mask, the n = floor(param*N
+ *        + 1/2) valid tokens of highest entropy (equal entropies: lower t
+ *        first) get 1, all others 0; param in [0, 1]
+ *
+ *   topk_logit  [T, K] fp32 teacher logits (device)
+ *   mask        [T] uint8 (1 = valid) or NULL (all valid); may alias mask_out
+ *   tau         temperature, finite and > 0
+ *   mask_out    [T] uint8 output (device)
+ *   entropy_out [T] fp32 output, or NULL
+ *   workspace   at least kd_entropy_filter_workspace_size(T) bytes,
+ *               256-byte aligned
+ * Entropies are computed in fp32, so a token whose entropy lies within
+ * fp32 rounding of the threshold (or of the kept set's boundary) may fall
+ * either way.  Returns KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED
+ * (K > KD_MAX_K, T*K >= 2^31), KD_ERR_WORKSPACE or KD_ERR_HIP.
+ */
+int kd_entropy_filter(const float *topk_logit, const uint8_t *mask, int64_t T,
+                      int32_t K, float tau, int32_t mode, float param,
+                      uint8_t *mask_out, float *entropy_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Kernel ids for kd_set_launch_log (bit i of the mask selects id i). */
 enum {
   KD_KERNEL_VALID_COUNT = 0, /* N = sum(mask), gradient and loss scales     */
@@ -198,7 +242,8 @@ enum {
   KD_KERNEL_TK_FILTER = 13,  /* logits of the other segments + candidates    */
   KD_KERNEL_TK_SELECT = 14,  /* exact top-K of each row's candidates         */
   KD_KERNEL_TK_STREAM = 15,  /* row-streaming top-K (generic path, overflow) */
-  KD_KERNEL_GRAD_CAST = 16   /* kd_grad_cast                                 */
+  KD_KERNEL_GRAD_CAST = 16,  /* kd_grad_cast                                 */
+  KD_KERNEL_ENTROPY_FILTER = 17 /* kd_entropy_filter (all of its kernels)    */
 };
 
 /* Largest supported K and hidden size of kd_teacher_topk. */

@@ -5,6 +5,7 @@ and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
 """
 from .kd_oracle import (  # noqa: F401
     dw_rows,
+    entropy_filter_mask,
     kd_topk_kl,
     log_softmax_rows,
     loss_given_lse,
@@ -12,5 +13,6 @@ from .kd_oracle import (  # noqa: F401
     rows_loss_and_dh,
     scattered_teacher,
     teacher_distribution,
+    teacher_entropy,
 )
 from .teacher_topk import teacher_logits, teacher_topk_cache  # noqa: F401

@@ -54,6 +54,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "teacher_entropy",
+    "entropy_filter_mask",
     "teacher_distribution",
     "log_softmax_rows",
     "kd_topk_kl",
@@ -267,3 +269,40 @@ def loss_given_lse(H, W, topk_idx, topk_logit, mask, tau, lse):
     row_loss = m * kl
     loss = tau * tau * row_loss.sum() / n_valid if n_valid > 0 else 0.0
     return loss, row_loss
+
+
+def teacher_entropy(topk_logit, tau):
+    """Entropy -sum_k q_k log q_k of the teacher distribution the loss uses
+    (R1: softmax of the K cached logits at temperature tau), fp64.  The
+    asibiont.com article, section "Distillation Token Filtering", scores each
+    token by the entropy of its teacher distribution; its implementation
+    sketch adds 1e-9 inside the log, which this exact form leaves out (q > 0
+    for finite logits)."""
+    lq, _ = log_softmax_rows(_f64(topk_logit) / float(tau))
+    return -(np.exp(lq) * lq).sum(axis=1)
+
+
+def entropy_filter_mask(topk_logit, mask, tau, mode, param):
+    """Token mask of the entropy filter (asibiont.com article, sections
+    "Distillation Token Filtering" and "A Concrete Implementation Sketch"):
+
+    * mode "above": valid and entropy > param (the sketch's
+      ``attention_mask.bool() & (entropy > entropy_threshold)``);
+    * mode "top_fraction": among the N valid tokens, the n = floor(param*N
+      + 1/2) with the highest entropy, equal entropies by lower index
+      ("keep a fixed percentage of tokens with the highest entropy").
+    """
+    ent = teacher_entropy(topk_logit, tau)
+    T = ent.shape[0]
+    valid = _mask_vector(mask, T) > 0
+    if mode == "above":
+        return (valid & (ent > float(param))).astype(np.uint8)
+    if mode != "top_fraction":
+        raise ValueError(mode)
+    n_valid = int(valid.sum())
+    n_keep = int(np.floor(float(np.float32(param)) * n_valid + 0.5))
+    order = np.lexsort((np.arange(T), -ent))
+    kept = [t for t in order if valid[t]][:n_keep]
+    out = np.zeros(T, dtype=np.uint8)
+    out[kept] = 1
+    return out

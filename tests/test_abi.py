@@ -228,3 +228,38 @@ def test_bwd_rejects_before_any_hip_call(kw, code):
 ])
 def test_grad_cast_rejects_before_any_hip_call(args, code):
     assert kd.load_library().kd_grad_cast(*args) == code
+
+
+# ------------------------------------------------------- entropy filter
+def _filter_call(**kw):
+    lib = kd.load_library()
+    a = dict(lg=1, mask=None, T=100, K=10, tau=1.0, mode=0, param=0.5, out=1,
+             ent=None, ws=256, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.kd_entropy_filter(a["lg"], a["mask"], a["T"], a["K"], a["tau"],
+                                 a["mode"], a["param"], a["out"], a["ent"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lg=None), kd.KD_ERR_INVALID_ARG),
+    (dict(out=None), kd.KD_ERR_INVALID_ARG),
+    (dict(T=0), kd.KD_ERR_INVALID_ARG),
+    (dict(K=0), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=0.0), kd.KD_ERR_INVALID_ARG),
+    (dict(mode=2), kd.KD_ERR_INVALID_ARG),
+    (dict(mode=1, param=1.5), kd.KD_ERR_INVALID_ARG),
+    (dict(mode=1, param=-0.1), kd.KD_ERR_INVALID_ARG),
+    (dict(param=float("nan")), kd.KD_ERR_INVALID_ARG),
+    (dict(K=2000), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=None), kd.KD_ERR_WORKSPACE),
+    (dict(ws_bytes=8), kd.KD_ERR_WORKSPACE),
+])
+def test_entropy_filter_rejects_before_any_hip_call(kw, code):
+    assert _filter_call(**kw) == code
+
+
+def test_entropy_filter_workspace_size():
+    assert kd.kd_entropy_filter_workspace_size(32768) == 256 + 32768 * 4
+    with pytest.raises(kd.KdError):
+        kd.kd_entropy_filter_workspace_size(0)

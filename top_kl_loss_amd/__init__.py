@@ -21,7 +21,9 @@ __all__ = [
     "kd_topk_kl_fwd_bwd", "kd_status_string", "kd_set_launch_log",
     "EXPORTED_SYMBOLS", "KERNEL_NAMES", "KD_TOPK_MAX_K", "KD_TOPK_MAX_D",
     "kd_teacher_topk_workspace_size", "kd_teacher_topk", "kd_topk_kl_fwd",
-    "kd_topk_kl_bwd", "kd_grad_cast",
+    "kd_topk_kl_bwd", "kd_grad_cast", "kd_entropy_filter",
+    "kd_entropy_filter_workspace_size", "KD_FILTER_ENTROPY_ABOVE",
+    "KD_FILTER_TOP_ENTROPY_FRACTION",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
@@ -35,12 +37,14 @@ KD_TOPK_MAX_D = 16384
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log",
                     "kd_teacher_topk_workspace_size", "kd_teacher_topk",
-                    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast")
+                    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast",
+                    "kd_entropy_filter_workspace_size", "kd_entropy_filter")
+KD_FILTER_ENTROPY_ABOVE, KD_FILTER_TOP_ENTROPY_FRACTION = 0, 1
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
                 "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
                 "scale_g", "transpose_w", "tk_sample", "tk_theta", "tk_filter",
-                "tk_select", "tk_stream", "grad_cast")
+                "tk_select", "tk_stream", "grad_cast", "entropy_filter")
 
 _lib = None
 
@@ -95,6 +99,12 @@ def load_library(path: str = LIB_PATH):
     lib.kd_grad_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int64,
                                  c.c_void_p, c.c_void_p]
     lib.kd_grad_cast.restype = c.c_int
+    lib.kd_entropy_filter_workspace_size.argtypes = [c.c_int64, c.POINTER(c.c_size_t)]
+    lib.kd_entropy_filter_workspace_size.restype = c.c_int
+    lib.kd_entropy_filter.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int64, c.c_int32, c.c_float, c.c_int32,
+        c.c_float, c.c_void_p, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    lib.kd_entropy_filter.restype = c.c_int
     lib.kd_status_string.argtypes = [c.c_int]
     lib.kd_status_string.restype = c.c_char_p
     lib.kd_set_launch_log.argtypes = [
@@ -364,3 +374,49 @@ def kd_teacher_topk(H, W, K, chunk=None, *, workspace=None, stream=None,
     if sync:
         hip.synchronize(stream)
     return ids, vals
+
+
+def kd_entropy_filter_workspace_size(T) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_entropy_filter_workspace_size(int(T), ctypes.byref(out)))
+    return out.value
+
+
+def kd_entropy_filter(topk_logit, mask=None, tau=1.0, mode="above", param=0.5,
+                      *, entropy=True, workspace=None, stream=None, sync=True):
+    """Token mask from the teacher's entropy over its K cached logits (see
+    the C header).  mode "above": keep valid tokens with entropy > param;
+    "top_fraction": keep round(param * N) valid tokens of highest entropy.
+    Returns (mask_out uint8 [T], entropy fp32 [T] or None)."""
+    import torch
+    lib = load_library()
+    codes = {"above": KD_FILTER_ENTROPY_ABOVE,
+             "top_fraction": KD_FILTER_TOP_ENTROPY_FRACTION}
+    if mode not in codes:
+        raise ValueError(f"mode must be one of {sorted(codes)}")
+    T, K = topk_logit.shape
+    if topk_logit.dtype != torch.float32 or not topk_logit.is_cuda or \
+            not topk_logit.is_contiguous():
+        raise ValueError("topk_logit must be a contiguous float32 CUDA tensor")
+    dev = topk_logit.device
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.numel() != T or mask.device != dev:
+            raise ValueError("mask must be uint8/bool [T] on the logits' device")
+        mask = mask.contiguous()
+    ws_bytes = kd_entropy_filter_workspace_size(T)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    out = torch.empty(T, dtype=torch.uint8, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
+    _enter(dev)
+    _check(lib.kd_entropy_filter(
+        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
+        T, K, float(tau), codes[mode], float(param), out.data_ptr(),
+        ent.data_ptr() if ent is not None else None, workspace.data_ptr(),
+        workspace.numel(), stream))
+    _leave(stream, sync)
+    return out, ent

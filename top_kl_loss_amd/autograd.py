@@ -21,7 +21,8 @@ from __future__ import annotations
 
 import torch
 
-from . import kd_grad_cast, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd
+from . import (kd_entropy_filter, kd_grad_cast, kd_topk_kl_bwd, kd_topk_kl_fwd,
+               kd_topk_kl_fwd_bwd)
 
 __all__ = ["TopKKLLossFunction", "topk_kl_loss", "TopKKLLoss"]
 
@@ -73,12 +74,21 @@ def _finish(g32, dtype, scale):
 
 
 def topk_kl_loss(H, W, topk_idx, topk_logit, mask=None, tau=1.0, chunk=None,
-                 recompute=False):
+                 recompute=False, entropy_filter=None):
     """tau^2 / N * sum_t mask_t KL(q_t || p_t): the teacher's distribution q
     over its K cached logits against the student's softmax p over all V
     logits z = H W^T, both at temperature tau (see include/kd_topk_kl.h).
     H [T,d], W [V,d] bf16 or fp32 CUDA tensors; topk_idx int32 and
-    topk_logit fp32 [T,K]; mask [T] or None.  Differentiable in H and W."""
+    topk_logit fp32 [T,K]; mask [T] or None.  Differentiable in H and W.
+
+    entropy_filter: None, ("above", threshold) or ("top_fraction", fraction):
+    the loss then runs only on the tokens kd_entropy_filter keeps (teacher
+    entropy above the threshold, or the given fraction of valid tokens with
+    the highest entropy), and N counts those tokens."""
+    if entropy_filter is not None:
+        mode, param = entropy_filter
+        mask, _ = kd_entropy_filter(topk_logit, mask, tau, mode, param,
+                                    entropy=False)
     return TopKKLLossFunction.apply(H, W, topk_idx, topk_logit, mask, tau,
                                     chunk, recompute)
 
@@ -86,10 +96,11 @@ def topk_kl_loss(H, W, topk_idx, topk_logit, mask=None, tau=1.0, chunk=None,
 class TopKKLLoss(torch.nn.Module):
     """Module form of topk_kl_loss with fixed tau, chunk and schedule."""
 
-    def __init__(self, tau=1.0, chunk=None, recompute=False):
+    def __init__(self, tau=1.0, chunk=None, recompute=False, entropy_filter=None):
         super().__init__()
         self.tau, self.chunk, self.recompute = float(tau), chunk, bool(recompute)
+        self.entropy_filter = entropy_filter
 
     def forward(self, H, W, topk_idx, topk_logit, mask=None):
         return topk_kl_loss(H, W, topk_idx, topk_logit, mask, self.tau,
-                            self.chunk, self.recompute)
+                            self.chunk, self.recompute, self.entropy_filter)

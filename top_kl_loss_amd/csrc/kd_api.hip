@@ -393,6 +393,49 @@ int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
   return KD_OK;
 }
 
+int kd_entropy_filter_workspace_size(int64_t T, size_t *bytes_out) {
+  if (!bytes_out || T < 1) return KD_ERR_INVALID_ARG;
+  if (T >= (int64_t(1) << 31)) return KD_ERR_UNSUPPORTED;
+  *bytes_out = align256(sizeof(uint64_t) * 2) + align256(sizeof(float) * (size_t)T);
+  return KD_OK;
+}
+
+int kd_entropy_filter(const float *topk_logit, const uint8_t *mask, int64_t T,
+                      int32_t K, float tau, int32_t mode, float param,
+                      uint8_t *mask_out, float *entropy_out, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!topk_logit || !mask_out || T < 1 || K < 1) return KD_ERR_INVALID_ARG;
+  if (!(tau > 0.f) || !isfinite(tau) || !isfinite(param)) return KD_ERR_INVALID_ARG;
+  if (mode != KD_FILTER_ENTROPY_ABOVE && mode != KD_FILTER_TOP_ENTROPY_FRACTION)
+    return KD_ERR_INVALID_ARG;
+  if (mode == KD_FILTER_TOP_ENTROPY_FRACTION && !(param >= 0.f && param <= 1.f))
+    return KD_ERR_INVALID_ARG;
+  if (K > KD_MAX_K || T >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31))
+    return KD_ERR_UNSUPPORTED;
+  size_t need = 0;
+  kd_entropy_filter_workspace_size(T, &need);
+  if (!workspace || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return KD_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  kd::FilterArgs a{};
+  a.topk_logit = topk_logit;
+  a.mask = mask;
+  a.T = T;
+  a.K = K;
+  a.inv_tau = 1.0f / tau;
+  a.mode = mode;
+  a.param = param;
+  a.sel = reinterpret_cast<uint64_t *>(ws);
+  a.entropy = entropy_out ? entropy_out
+                          : reinterpret_cast<float *>(ws + align256(sizeof(uint64_t) * 2));
+  a.mask_out = mask_out;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = logged(KD_KERNEL_ENTROPY_FILTER, s,
+                              [&] { return kd::launch_entropy_filter(a, s); });
+  return e == hipSuccess ? KD_OK : hip_fail(e);
+}
+
 int kd_set_launch_log(uint32_t kernel_mask, void *const *start_events,
                       void *const *end_events, int32_t *kinds,
                       int32_t capacity, int32_t *count) {

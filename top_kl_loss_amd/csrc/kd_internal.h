@@ -140,6 +140,22 @@ struct TkArgs {
   int all_rows;      // row-streaming kernel: every row, not only overflows
 };
 
+// ---------------------------------------------------------------------------
+// Entropy-based token filter over the cached teacher top-K.
+struct FilterArgs {
+  const float *topk_logit;  // [T, K]
+  const uint8_t *mask;      // [T] or null (all valid)
+  int64_t T;
+  int K;
+  float inv_tau;
+  int mode;                 // 0: entropy > param; 1: top fraction param
+  float param;
+  float *entropy;           // [T] teacher entropy (output or workspace)
+  uint8_t *mask_out;        // [T]
+  uint64_t *sel;            // [2] workspace: selection key, kept count
+};
+hipError_t launch_entropy_filter(const FilterArgs &a, hipStream_t s);
+
 hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s);
 hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s);
 hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s);
