@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
     if (t < a.C) {
       u32x4 *src = reinterpret_cast<u32x4 *>(P + (size_t)t * a.ldp + v0) + c;
       v = Elem<uint16_t>::scale(*src, a.fseg[(size_t)t * a.nseg + seg]);
-      *src = v;
+      __builtin_nontemporal_store(v, src);  // streamed: read once by dH
     }
     *reinterpret_cast<u32x4 *>(&g_s[r][c * 8]) = v;
   }
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
       o[p] = uint32_t(g_s[q * 8 + 2 * p][vr]) | (uint32_t(g_s[q * 8 + 2 * p + 1][vr]) << 16);
-    reinterpret_cast<u32x4 *>(a.Gt + (size_t)(v0 + vr) * a.ldh + t0)[q] = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(a.Gt + (size_t)(v0 + vr) * a.ldh + t0) + q);
   }
 }
 
