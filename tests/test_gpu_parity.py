@@ -156,3 +156,11 @@ def test_bf16_tuned_path_with_transposed_weight_copy():
     x = synth.make_case("bf16_wt", case=32, T=600, d=192, V=3001, K=50,
                         dtype="bf16", tau=1.1, mask_frac=0.05, chunk=256)
     check_case(x)
+
+
+def test_bf16_tuned_path_wide_tiles_with_transposed_weight_copy():
+    # d a multiple of 320: the dH and dW GEMMs use 256 x 320 tiles (dH with
+    # the W^T copy since chunk >= d); ragged T, V, padding rows
+    x = synth.make_case("bf16_wide", case=33, T=900, d=640, V=3001, K=64,
+                        dtype="bf16", tau=1.2, mask_frac=0.05, chunk=640)
+    check_case(x)

@@ -52,6 +52,7 @@ struct Layout {
   size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
       o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt;
   bool wt;
+  int dh_bn, dw_bn;
   int ldh;
   size_t total;
 };
@@ -77,7 +78,13 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
   L.ldp = L.nseg * kd::SEG;
   L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, L.ldp);
-  L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast);
+  // A W^T copy (V x d bf16) lets the dH GEMM copy both operands by DMA; it is
+  // kept only when it is no larger than one slice's G (C >= d), so the extra
+  // memory stays bounded by a slice.
+  L.wt = L.fast && (int64_t)L.C >= d;
+  L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;
+  L.dh_bn = L.wt ? L.dw_bn : 256;  // the register path of dH is square only
+  L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast, L.dh_bn);
   L.esize = dtype == KD_BF16 ? 2 : 4;
   const size_t C = L.C, nseg = L.nseg;
   size_t o = 0;
@@ -99,10 +106,6 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.ldh = (int)((C + 63) / 64 * 64);
   L.o_ht = take(L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0);
   L.o_gt = take(L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0);
-  // A W^T copy (V x d bf16) lets the dH GEMM copy both operands by DMA; it is
-  // kept only when it is no larger than one slice's G (C >= d), so the extra
-  // memory stays bounded by a slice.
-  L.wt = L.fast && (int64_t)L.C >= d;
   L.o_wt = take(L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0);
   L.total = o;
   return L;
@@ -242,6 +245,8 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
   a.dW = dW;
   a.fast = L.fast ? 1 : 0;
   a.need_grad = grads ? 1 : 0;
+  a.dh_bn = L.dh_bn;
+  a.dw_bn = L.dw_bn;
   a.lse_out = lse_out;
 
   hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {

@@ -453,8 +453,8 @@ bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp) {
          (C + 512) * ldp * 2 < lim && (C + 512) * d * 2 < lim;
 }
 
-int dh_splits(int C, int d, int nseg, bool fast) {
-  if (fast) return fast_dh_splits(C, d, nseg);
+int dh_splits(int C, int d, int nseg, bool fast, int bn) {
+  if (fast) return fast_dh_splits(C, d, nseg, bn);
   const int tiles = ((C + DH_BM - 1) / DH_BM) * ((d + DH_BN - 1) / DH_BN);
   int s = (1024 + tiles - 1) / tiles;
   if (s < 1) s = 1;

@@ -158,33 +158,34 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
 // ---------------------------------------------------------------- dH GEMM
 // A = G (K-contiguous over the vocabulary; copied by DMA).  B = W^T by DMA
 // when the call keeps a W^T copy, else W (vocabulary rows, hidden columns)
-// transposed through registers.
+// transposed through registers (square tiles only).
+template <class CF>
 __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / CF::WN, wn = wave % CF::WN;
   const int nmt = (a.C + BM - 1) / BM;
-  const int nnt = (a.d + BN - 1) / BN;
+  const int nnt = (a.d + CF::BN - 1) / CF::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int split = tile / (nnt * nmt);
   int mt, nt;
   group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int m0 = mt * BM, n0 = nt * CF::BN;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
   const int kbeg = sbeg * SEG, kend = send * SEG;
   CopyK<8> ca;
   ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-  f32x16 acc[TM][TN];
+  f32x16 acc[CF::TM][CF::TN];
   zero_acc(acc);
   const int nk = (kend - kbeg) / BK;
-  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  const int ar = wm * CF::WTM + (lane & 31), br = wn * CF::WTN + (lane & 31), hh = lane >> 5;
   if (a.Wt) {
     // B = W^T (hidden rows, vocabulary contiguous): both operands by DMA
-    CopyK<8> cb;
+    CopyK<8, CF::BN> cb;
     cb.init(a.Wt, (uint64_t)a.d * a.ldp * 2, a.ldp, n0, wave, lane);
     nt_loop(ca, cb, kbeg, nk, lds, ar, br, hh, acc);
-  } else {
+  } else if constexpr (CF::BN == BN) {
     // B = W (vocabulary rows, hidden contiguous) through registers
     RegMN4 rb;
     rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
@@ -207,13 +208,13 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
 
   float *out = a.dh_part + (size_t)split * a.dh_stride;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+    for (int j = 0; j < CF::TN; ++j) {
+      const int col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + i * 32 + acc_row(e, lane);
+        const int row = m0 + wm * CF::WTM + i * 32 + acc_row(e, lane);
         if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
       }
     }
@@ -221,33 +222,35 @@ __global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
 
 // ---------------------------------------------------------------- dW GEMM
 // A = G^T, B = H_c^T (both K-contiguous over the slice's tokens; DMA).
+template <class CF>
 __global__ __launch_bounds__(NT, 1) void k_fast_dw(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int nnt = (a.d + BN - 1) / BN;
+  const int wm = wave / CF::WN, wn = wave % CF::WN;
+  const int nnt = (a.d + CF::BN - 1) / CF::BN;
   const int nmt = (a.V + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   int mt, nt;
   group_tile(tile, nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
-  CopyK<8> ca, cb;
+  const int m0 = mt * BM, n0 = nt * CF::BN;
+  CopyK<8> ca;
+  CopyK<8, CF::BN> cb;
   ca.init(a.Gt, (uint64_t)a.ldp * a.ldh * 2, a.ldh, m0, wave, lane);
   cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave, lane);
 
-  f32x16 acc[TM][TN];
+  f32x16 acc[CF::TM][CF::TN];
   zero_acc(acc);
-  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  const int ar = wm * CF::WTM + (lane & 31), br = wn * CF::WTN + (lane & 31), hh = lane >> 5;
   nt_loop(ca, cb, 0, (a.C + BK - 1) / BK, lds, ar, br, hh, acc);
 
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+    for (int j = 0; j < CF::TN; ++j) {
+      const int col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + i * 32 + acc_row(e, lane);
+        const int row = m0 + wm * CF::WTM + i * 32 + acc_row(e, lane);
         if (row < a.V && col < a.d) {
           float *p = a.dW + (size_t)row * a.d + col;
           // exactly one addition per element and slice, slices in stream
@@ -334,25 +337,42 @@ __global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
 }
 
 template <typename K>
-hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s) {
+hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds = LDS_BYTES) {
   if (grid <= 0) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Splits of the vocabulary contraction of dH: about three full rounds of
-// one workgroup per CU.
-int fast_dh_splits(int C, int d, int nseg) {
-  const int tiles = ((C + BM - 1) / BM) * ((d + BN - 1) / BN);
-  int s = (768 + tiles - 1) / tiles;
-  if (s < 1) s = 1;
-  if (s > nseg) s = nseg;
-  return s;
+int fast_bn(int d) { return best_bn(d); }
+
+// Splits of the vocabulary contraction of dH.  Each split is one workgroup
+// per output tile, run in rounds over the 256 CUs (one workgroup per CU), so
+// the time is about ceil(tiles * s / 256) rounds of 1/s of a tile's whole
+// contraction, plus the s partial sums written and read back by the
+// reduction.  The rates below only weigh the two terms (a tile at ~45% of
+// the matrix-core peak of one CU; partials at ~4.5 TB/s).
+int fast_dh_splits(int C, int d, int nseg, int bn) {
+  constexpr int NCU = 256;
+  const int tiles = ((C + BM - 1) / BM) * ((d + bn - 1) / bn);
+  const double tile_s = 2.0 * BM * bn * (double)nseg * SEG / 4.4e12;
+  const double part_s = (double)C * d * 4.0 / 4.5e12;
+  const int smax = nseg < 64 ? nseg : 64;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= smax; ++sp) {
+    const double rounds = (double)((tiles * sp + NCU - 1) / NCU);
+    const double cost = rounds * tile_s / sp + (sp + 1) * part_s;
+    if (cost < best_cost * (1.0 - 1e-9)) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
@@ -360,7 +380,11 @@ hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
-  return launch(k_fast_dh, ((a.C + BM - 1) / BM) * ((a.d + BN - 1) / BN) * a.splits, a, s);
+  const int nmt = (a.C + BM - 1) / BM;
+  if (a.dh_bn == WideCfg::BN)
+    return launch(k_fast_dh<WideCfg>, nmt * ((a.d + WideCfg::BN - 1) / WideCfg::BN) * a.splits,
+                  a, s, WideCfg::LDS);
+  return launch(k_fast_dh<SquareCfg>, nmt * ((a.d + BN - 1) / BN) * a.splits, a, s);
 }
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
@@ -385,7 +409,11 @@ hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
-  return launch(k_fast_dw, ((a.V + BM - 1) / BM) * ((a.d + BN - 1) / BN), a, s);
+  const int nmt = (a.V + BM - 1) / BM;
+  if (a.dw_bn == WideCfg::BN)
+    return launch(k_fast_dw<WideCfg>, nmt * ((a.d + WideCfg::BN - 1) / WideCfg::BN), a, s,
+                  WideCfg::LDS);
+  return launch(k_fast_dw<SquareCfg>, nmt * ((a.d + BN - 1) / BN), a, s);
 }
 
 }  // namespace kd

@@ -29,6 +29,28 @@ constexpr int OP_BYTES = 256 * 128;          // one operand tile per stage
 constexpr int STAGE_BYTES = 2 * OP_BYTES;    // A then B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // 128 KiB
 
+// Tile shapes with 256 rows of A: 8 waves as (8/WN_) x WN_, each wave
+// TM_ x TN_ blocks of 32 x 32.  Square: 256 x 256 (the default above);
+// Wide: 256 x 320 for N = d multiple of 320 (d = 2880 = 9 x 320 wastes no
+// MFMA work on padding, where 256-wide tiles waste 6.25%).
+template <int WN_, int TM_, int TN_>
+struct TileCfg {
+  static constexpr int WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int WTM = TM_ * 32, WTN = TN_ * 32;
+  static constexpr int BN = WN_ * WTN;
+  static constexpr int LDS = 2 * (256 + BN) * 128;
+  static_assert((8 / WN_) * WTM == 256, "256 rows of A");
+};
+using SquareCfg = TileCfg<4, 4, 2>;
+using WideCfg = TileCfg<2, 2, 5>;
+static_assert(WideCfg::BN == 320 && WideCfg::LDS <= 160 * 1024, "wide tile");
+
+// Width of the N tile that wastes the least MFMA work on a dimension of n.
+inline int best_bn(int n) {
+  const int w256 = (n + 255) / 256 * 256 - n, w320 = (n + 319) / 320 * 320 - n;
+  return w320 < w256 ? 320 : 256;
+}
+
 typedef __attribute__((address_space(3))) void *lds_vptr;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -44,11 +66,12 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 
 // ------------------------------------------------------------- operand copy
 // K-contiguous operand, element (mn, k) at byte (mn * ld + k) * 2 of `res`,
-// copied by NW waves (index w among them), each issuing 32/NW instructions
-// of 1 KiB (8 rows x 128 B) per k-step.
-template <int NW>
+// ROWS rows copied by NW waves (index w among them), each issuing
+// ROWS/8/NW instructions of 1 KiB (8 rows x 128 B) per k-step.
+template <int NW, int ROWS = 256>
 struct CopyK {
-  static constexpr int N = 32 / NW;
+  static constexpr int N = ROWS / 8 / NW;
+  static_assert(N * 8 * NW == ROWS, "rows per wave");
   __amdgpu_buffer_rsrc_t res;
   uint32_t off[N];
   int w;
@@ -135,11 +158,12 @@ __device__ __forceinline__ int acc_row(int e, int lane) {
   return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
+template <int TM_, int TN_>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM_][TN_]) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM_; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN_; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
@@ -148,37 +172,39 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
 // fragments are read from LDS while group g's MFMAs run.  The scheduling
 // barriers pin the order (one MFMA, one fragment read, ...) that keeps the
 // matrix pipe fed; the compiler's own order serialises reads and MFMAs.
+template <int TM_, int TN_>
 __device__ __forceinline__ void kstep(const char *ta, const char *tb, int ar, int br, int h,
-                                      f32x16 (&acc)[TM][TN]) {
-  constexpr int NRD = TM + TN;  // fragment reads per group
-  u32x4 fa[2][TM], fb[2][TN];
+                                      f32x16 (&acc)[TM_][TN_]) {
+  constexpr int NRD = TM_ + TN_;  // fragment reads per group
+  static_assert(TM_ * TN_ >= NRD, "more reads than MFMAs per group");
+  u32x4 fa[2][TM_], fb[2][TN_];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = frag(ta, ar + i * 32, 0, h);
+  for (int i = 0; i < TM_; ++i) fa[0][i] = frag(ta, ar + i * 32, 0, h);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) fb[0][j] = frag(tb, br + j * 32, 0, h);
+  for (int j = 0; j < TN_; ++j) fb[0][j] = frag(tb, br + j * 32, 0, h);
   __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int c = g & 1;
     if (g < 3) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = frag(ta, ar + i * 32, g + 1, h);
+      for (int i = 0; i < TM_; ++i) fa[c ^ 1][i] = frag(ta, ar + i * 32, g + 1, h);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = frag(tb, br + j * 32, g + 1, h);
+      for (int j = 0; j < TN_; ++j) fb[c ^ 1][j] = frag(tb, br + j * 32, g + 1, h);
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM_; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) mfma(acc[i][j], fa[c][i], fb[c][j]);
+      for (int j = 0; j < TN_; ++j) mfma(acc[i][j], fa[c][i], fb[c][j]);
     if (g < 3) {
 #pragma unroll
       for (int r = 0; r < NRD; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NRD, 0);
+      if (TM_ * TN_ > NRD) __builtin_amdgcn_sched_group_barrier(0x008, TM_ * TN_ - NRD, 0);
     } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, TM_ * TN_, 0);
     }
   }
 }
@@ -205,20 +231,25 @@ __device__ __forceinline__ void group_tile(int L, int nm, int nn, int gm_max, in
 
 // Main loop of an NT product (both operands K-contiguous, copied by DMA):
 // nk k-steps starting at contraction index kbeg.
-__device__ __forceinline__ void nt_loop(CopyK<8> &ca, CopyK<8> &cb, int kbeg, int nk, char *lds,
-                                        int ar, int br, int hh, f32x16 (&acc)[TM][TN]) {
+// nk k-steps starting at contraction index kbeg; a stage holds RA rows of A
+// then RB rows of B (128 bytes each).
+template <int RA, int RB, int TM_, int TN_>
+__device__ __forceinline__ void nt_loop(CopyK<8, RA> &ca, CopyK<8, RB> &cb, int kbeg, int nk,
+                                        char *lds, int ar, int br, int hh,
+                                        f32x16 (&acc)[TM_][TN_]) {
+  constexpr int OPA = RA * 128, ST = (RA + RB) * 128;
   ca.issue(lds, kbeg);
-  cb.issue(lds + OP_BYTES, kbeg);
+  cb.issue(lds + OPA, kbeg);
   for (int ks = 0; ks < nk; ++ks) {
-    const char *cur = lds + (ks & 1) * STAGE_BYTES;
-    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+    const char *cur = lds + (ks & 1) * ST;
+    char *nxt = lds + ((ks + 1) & 1) * ST;
     // the last step re-copies itself into the idle stage (never read)
     const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
     wait_vm0();
     __syncthreads();
     ca.issue(nxt, kn);
-    cb.issue(nxt + OP_BYTES, kn);
-    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+    cb.issue(nxt + OPA, kn);
+    kstep(cur, cur + OPA, ar, br, hh, acc);
   }
   wait_vm0();
 }
