@@ -92,15 +92,19 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     const int sr = tid / TPR, part = tid % TPR;
     const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
     const int cb0 = part * CPT;
+    // base-2 units: v = z / tau * log2(e), P = 2^(v - max v); only the
+    // vocabulary's last segment has columns past V (excluded)
     float v[CPT];
     float mx = -INFINITY;
+    const float s2 = a.inv_tau * LOG2E;
+    const bool tail = n0 + BN > a.V;
 #pragma unroll
     for (int c = 0; c < CPT; c += 4) {
       const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + cb0 + c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ok = n0 + cb0 + c + u < a.V;
-        v[c + u] = ok ? z[u] * a.inv_tau : -INFINITY;
+        v[c + u] = z[u] * s2;
+        if (tail && n0 + cb0 + c + u >= a.V) v[c + u] = -INFINITY;
         mx = fmaxf(mx, v[c + u]);
       }
     }
@@ -109,10 +113,12 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const float p = v[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((v[c] - mx) * LOG2E);
+      // exp2(-inf) = 0 covers the excluded columns
+      const float p = __builtin_amdgcn_exp2f(v[c] - mx);
       v[c] = p;
       sum += p;
     }
+    mx *= LN2;  // the segment maximum of z / tau
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
     if (r < a.C) {
