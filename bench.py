@@ -44,8 +44,8 @@ _TK_SRC = ("kd_teacher.hip", "kd_mfma_tile.h", "kd_select.h", "kd_device.h",
            "kd_internal.h")
 TRAFFIC_KERNELS = {
     "loss": [("k_fast_logits(", "gemm_logits", _GEMM_SRC),
-             ("k_fast_dh(", "gemm_dh", _GEMM_SRC),
-             ("k_fast_dw(", "gemm_dw", _GEMM_SRC),
+             ("k_fast_dh", "gemm_dh", _GEMM_SRC),
+             ("k_fast_dw", "gemm_dw", _GEMM_SRC),
              ("k_scale_g(", "scale_g", _GEMM_SRC),
              ("k_transpose_w(", "transpose_w", _GEMM_SRC),
              ("k_transpose_h(", "transpose_h", _GEMM_SRC),
