@@ -131,3 +131,18 @@ def test_autograd_loss_with_an_entropy_filter():
     G.assert_loss_close(float(loss.item()), ref["loss"], "f32")
     G.assert_grad_close(G.to_np(H.grad), ref["dH"], "f32", "H.grad")
     G.assert_grad_close(G.to_np(W.grad), ref["dW"], "f32", "W.grad")
+
+
+def test_top_fraction_with_structured_entropies():
+    # every 16th token (offset 8) gets the maximal entropy (equal logits):
+    # a strongly structured entropy sequence; the selection is still exact
+    T, K = 4096, 16
+    rng = np.random.default_rng(76)
+    lg = np.ascontiguousarray(rng.standard_normal((T, K)) * 3, dtype=np.float32)
+    lg[8::16] = 0.0
+    out, ent = _run(lg, None, 1.0, "top_fraction", 0.5)
+    want = orc.entropy_filter_mask(lg, None, 1.0, "top_fraction", 0.5)
+    assert int(out.sum()) == int(want.sum()) == 2048
+    assert np.all(out[8::16] == 1)          # the maximal-entropy tokens
+    o_ent = orc.teacher_entropy(lg, 1.0)
+    assert o_ent[out == 1].min() >= o_ent[out == 0].max() - 2 * ENT_TOL
