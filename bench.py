@@ -140,6 +140,28 @@ def record_traffic(op, config_key, fetch_dir, write_dir, copy_bytes):
     log(f"traffic of {sorted(out)} written to {TRAFFIC_FILE}")
 
 
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def peak_from_device(hip):
+    """bf16 dense peak from the device's CU count and peak clock
+    (4096 flop per clock per CU for bf16 MFMA on gfx950)."""
+    cus = hip.device_attribute(hip.ATTR_MULTIPROCESSOR_COUNT)
+    khz = hip.device_attribute(hip.ATTR_CLOCK_RATE_KHZ)
+    return {"cus": cus, "clock_mhz": khz / 1e3,
+            "bf16_tflops": round(cus * khz * 1e3 * 4096 / 1e12, 1)}
+
+
 def cpu_baseline(x, target_s):
     """The oracle, as it stands, on the first R tokens of the workload."""
     import numpy as np
@@ -166,8 +188,9 @@ def cpu_baseline(x, target_s):
     R = int(max(32, min(x.T, 4096, (target_s - fixed) / per)))
     log(f"cpu baseline: oracle on {R} tokens (~{fixed + per * R:.0f} s)")
     dt = run(R)
+    model, affinity = cpu_info()
     return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "affinity_cpus": affinity,
             "sample": f"first {R} of {x.T} tokens of {x.name} "
                       f"(full d={x.d}, V={x.V}, K={x.K}), fp64 NumPy, one "
                       f"chunk; {dt:.1f} s wall"}
@@ -344,12 +367,15 @@ def main():
     kinds = (ctypes.c_int32 * cap)()
     count = ctypes.c_int32(0)
     kd.kd_set_launch_log(1 << dom, arr_s, arr_e, kinds, cap, ctypes.byref(count))
+    step_ev = [hip.Event() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     hip.synchronize()
     log(f"timing {args.steps} step(s)")
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        step_ev[i].record(stream.value)
         step()
+    step_ev[args.steps].record(stream.value)
     stream.synchronize()
     t_end = time.perf_counter()
     torch.cuda.synchronize()
@@ -358,6 +384,13 @@ def main():
     ms_step = wall * 1e3 / args.steps
     dom_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
     dom_avg = sum(dom_ms) / len(dom_ms)
+    per_step = sorted(step_ev[i].elapsed_ms(step_ev[i + 1]) for i in range(args.steps))
+    # device memory in use around one more call: the library allocates nothing
+    hip.synchronize()
+    free0, total = hip.mem_get_info()
+    step()
+    stream.synchronize()
+    free1, _ = hip.mem_get_info()
 
     flops_step = (2.0 if args.op == "fwd" else 6.0) * T * d * V
     tflops = flops_step / (ms_step * 1e-3) / 1e12
@@ -395,6 +428,12 @@ def main():
         "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
         "extra_hbm_bytes": ws_bytes,
         "dense_extra_hbm_bytes": 8 * T * V,
+        "hbm": {"workspace_bytes": ws_bytes,
+                "device_used_delta_during_call_bytes": int(free0 - free1),
+                "device_total_bytes": int(total)},
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 3),
+                    "min": round(per_step[0], 3)},
+        "peak_from_device": peak_from_device(hip),
         "loss": lval,
         "kernel_ms_one_step": split,
         "roofline": roof,
@@ -432,8 +471,9 @@ def cpu_baseline_teacher(x, K, target_s):
     R = int(max(16, min(x.T, 4096, (target_s - fixed) / per)))
     log(f"cpu baseline: teacher oracle on {R} rows (~{fixed + per * R:.0f} s)")
     dt = run(R)
+    model, affinity = cpu_info()
     return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "affinity_cpus": affinity,
             "sample": f"first {R} of {x.T} rows of {x.name} (full d={x.d}, "
                       f"V={x.V}, K={K}), fp64 NumPy matmul + per-row "
                       f"lexsort; {dt:.1f} s wall"}

@@ -34,6 +34,8 @@ def runtime():
     h.hipEventDestroy.argtypes = [vp]
     h.hipGetErrorString.argtypes = [ctypes.c_int]
     h.hipGetErrorString.restype = ctypes.c_char_p
+    h.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    h.hipMemGetInfo.argtypes = [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     _hip = h
     return h
 
@@ -42,6 +44,24 @@ def check(err):
     if err != 0:
         msg = runtime().hipGetErrorString(err).decode()
         raise RuntimeError(f"HIP error {err}: {msg}")
+
+
+# hipDeviceAttribute_t values of the runtime's header
+ATTR_CLOCK_RATE_KHZ = 5        # hipDeviceAttributeClockRate
+ATTR_MULTIPROCESSOR_COUNT = 63  # hipDeviceAttributeMultiprocessorCount
+
+
+def device_attribute(attr: int, device: int = 0) -> int:
+    v = ctypes.c_int(0)
+    check(runtime().hipDeviceGetAttribute(ctypes.byref(v), int(attr), int(device)))
+    return v.value
+
+
+def mem_get_info():
+    """(free, total) bytes of the current device."""
+    free, total = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    check(runtime().hipMemGetInfo(ctypes.byref(free), ctypes.byref(total)))
+    return free.value, total.value
 
 
 def set_device(index: int):
