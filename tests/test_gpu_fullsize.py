@@ -84,6 +84,16 @@ def test_t4k_exact_loss_all_rows_and_sampled_gradients():
                        lse, vs)
     G.assert_grad_close(G.to_np(dW[vs]), o_dw, x.dtype, "sampled dW rows")
     _check_identities(x, dev, dH, dW)
+    # the forward-only entry point: the same loss bitwise, and every row's
+    # logsumexp against the oracle's
+    import top_kl_loss_amd as kd
+    f_loss, f_rl, f_lse = kd.kd_topk_kl_fwd(dev["H"], dev["W"], dev["topk_idx"],
+                                            dev["topk_logit"], dev["mask"],
+                                            x.tau, x.chunk)
+    assert float(f_loss.item()) == float(loss.item())
+    assert np.array_equal(G.to_np(f_rl), G.to_np(rl))
+    err = np.abs(G.to_np(f_lse) - lse).max() / np.abs(lse).max()
+    assert err <= 1e-5, f"lse max rel {err:.2e}"
 
 
 def test_t8k_masked_sampled_rows_and_identities():

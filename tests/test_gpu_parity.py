@@ -164,3 +164,10 @@ def test_bf16_tuned_path_wide_tiles_with_transposed_weight_copy():
     x = synth.make_case("bf16_wide", case=33, T=900, d=640, V=3001, K=64,
                         dtype="bf16", tau=1.2, mask_frac=0.05, chunk=640)
     check_case(x)
+
+
+def test_bf16_tuned_path_largest_k():
+    # K = KD_MAX_K = 1024 teacher slots per row on the tuned path
+    x = synth.make_case("bf16_kmax", case=34, T=300, d=128, V=5000, K=1024,
+                        dtype="bf16", tau=1.0, mask_frac=0.05, chunk=128)
+    check_case(x)
