@@ -74,15 +74,19 @@ enum {
 
 /*
  * kd_topk_kl_workspace_size -- bytes of scratch device memory needed by
- * kd_topk_kl_fwd_bwd for these sizes.
+ * kd_topk_kl_fwd_bwd, kd_topk_kl_fwd and kd_topk_kl_bwd for these sizes.
  *
  * The workspace holds the per-slice intermediates of the chunked loss
  * ("Making Knowledge Distillation Cheap Enough to Run at Scale", aipuls.nl,
  * section "Summary": memory bounded by one slice): the slice's shifted
- * student probabilities (chunk x V, in the input element type), per-row
- * and per-vocabulary-segment softmax statistics, the teacher distribution
- * of the slice, split-K partial sums of dH for the slice, and O(T) per-row
- * scalars.  It grows with chunk*V and chunk*d, never with T*V.
+ * student probabilities, then its logit gradient (chunk x V, in the input
+ * element type), per-row and per-vocabulary-segment softmax statistics,
+ * the teacher distribution of the slice, split-K partial sums of dH for the
+ * slice and O(T) per-row scalars; on the tuned bf16 path also the
+ * transposed gradient (V x chunk) and hidden states (d x chunk) of the
+ * slice and, when chunk >= d, one transposed copy of W (d x V bf16, no
+ * larger than the slice's gradient).  It grows with chunk*V and chunk*d,
+ * never with T*V.
  *
  * Arguments: sizes as for kd_topk_kl_fwd_bwd; `chunk` is clamped to [1, T].
  * `bytes_out` (host pointer) receives the size.  Returns KD_OK,
