@@ -52,7 +52,13 @@ __global__ __launch_bounds__(256) void k_entropy_rows(FilterArgs a) {
 // One workgroup: N = number of valid tokens, n_keep = floor(param * N +
 // 1/2), and the n_keep-th smallest key (entropy descending, token index
 // ascending) among the valid tokens.
+// Up to ENT_LDS_ROWS tokens keep the high words of their keys in LDS for
+// the selection's passes; longer batches read them from memory each pass.
+constexpr int ENT_LDS_ROWS = 32768;
+
+template <bool IN_LDS>
 __global__ __launch_bounds__(256) void k_entropy_select(FilterArgs a) {
+  extern __shared__ uint32_t khi[];  // [T] when IN_LDS
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sc[8];
   __shared__ uint64_t res;
@@ -60,7 +66,11 @@ __global__ __launch_bounds__(256) void k_entropy_select(FilterArgs a) {
   const uint8_t *mask = a.mask;
   const float *ent = a.entropy;
   uint32_t cnt = 0;
-  for (int64_t t = tid; t < a.T; t += 256) cnt += mask ? (mask[t] != 0) : 1u;
+  for (int64_t t = tid; t < a.T; t += 256) {
+    const bool valid = mask ? (mask[t] != 0) : true;
+    cnt += valid;
+    if (IN_LDS) khi[t] = valid ? key_hi(ent[t]) : 0xffffffffu;
+  }
   const uint32_t n_valid = block_incl_scan(cnt, sc);  // thread 255 holds the total
   __syncthreads();
   if (tid == 255) sc[7] = n_valid;
@@ -70,11 +80,17 @@ __global__ __launch_bounds__(256) void k_entropy_select(FilterArgs a) {
   __syncthreads();
   uint64_t kappa = 0;
   if (n_keep > 0) {
-    auto key_at = [mask, ent](int i) {
-      const bool valid = mask ? mask[i] != 0 : true;
-      return valid ? make_key(ent[i], i) : ~0ull;
-    };
-    kappa = block_select(key_at, (int)a.T, (int)(n_keep - 1), hist, sc, &res);
+    if (IN_LDS) {
+      // padding tokens: high word 0xffffffff, above every valid key
+      auto key_at = [](int i) { return (uint64_t(khi[i]) << 32) | uint32_t(i); };
+      kappa = block_select(key_at, (int)a.T, (int)(n_keep - 1), hist, sc, &res);
+    } else {
+      auto key_at = [mask, ent](int i) {
+        const bool valid = mask ? mask[i] != 0 : true;
+        return valid ? make_key(ent[i], i) : ~0ull;
+      };
+      kappa = block_select(key_at, (int)a.T, (int)(n_keep - 1), hist, sc, &res);
+    }
   }
   if (tid == 0) {
     a.sel[0] = kappa;
@@ -82,7 +98,9 @@ __global__ __launch_bounds__(256) void k_entropy_select(FilterArgs a) {
   }
 }
 
-// mask_out[t] = mask[t] && key(t) <= kappa (and n_keep > 0).
+// mask_out[t] = mask[t] && key(t) <= kappa (and n_keep > 0).  A padding
+// token's key in the selection ranks after every valid key, and padding is
+// never kept, so both key forms agree here.
 __global__ __launch_bounds__(256) void k_entropy_apply(FilterArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= a.T) return;
@@ -98,7 +116,15 @@ hipError_t launch_entropy_filter(const FilterArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_entropy_rows, dim3(g), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.mode == 0) return e;
-  hipLaunchKernelGGL(k_entropy_select, dim3(1), dim3(256), 0, s, a);
+  if (a.T <= ENT_LDS_ROWS) {
+    const int lds = (int)(a.T * sizeof(uint32_t));
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_entropy_select<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_entropy_select<true>, dim3(1), dim3(256), lds, s, a);
+  } else {
+    hipLaunchKernelGGL(k_entropy_select<false>, dim3(1), dim3(256), 0, s, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_entropy_apply, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -176,10 +176,25 @@ __global__ __launch_bounds__(256) void k_tk_theta(TkArgs a) {
   const int sstride = a.sstride;
   const float *src = a.zs + (size_t)r * a.ldzs;
   auto id_of = [sstride](int i) { return (i / SEG) * sstride * SEG + (i % SEG); };
-  for (int i = tid; i < n; i += 256) {
-    const int id = id_of(i);
-    // entries past the vocabulary rank after every real entry
-    hi[i] = id < a.V ? key_hi(src[i]) : 0xffffffffu;
+  // n is a multiple of 256 (ns segments): 16-byte loads, all of a thread's
+  // loads in flight before their use
+  constexpr int U = TK_NSAMPLE * SEG / 1024;
+  f32x4 zv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = (u * 256 + tid) * 4;
+    if (i < n) zv[u] = *reinterpret_cast<const f32x4 *>(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = (u * 256 + tid) * 4;
+    if (i < n) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // entries past the vocabulary rank after every real entry
+        hi[i + c] = id_of(i + c) < a.V ? key_hi(zv[u][c]) : 0xffffffffu;
+      }
+    }
   }
   if (tid == 0) nc = 0;
   __syncthreads();
@@ -213,7 +228,22 @@ __global__ __launch_bounds__(256) void k_tk_select(TkArgs a) {
   const int cnt = a.cnt[r];
   const int n = cnt < a.cap ? cnt : a.cap;
   const uint64_t *src = a.cand + (size_t)r * a.cap;
-  for (int i = tid; i < n; i += 256) keys[i] = src[i];
+  // 16-byte loads, eight in flight per thread
+  for (int base = 0; base < n; base += 256 * 16) {
+    u32x4 kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + (u * 256 + tid) * 2;
+      if (i + 1 < n) kv[u] = *reinterpret_cast<const u32x4 *>(src + i);
+      else if (i < n) kv[u] = u32x4{uint32_t(src[i]), uint32_t(src[i] >> 32), 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + (u * 256 + tid) * 2;
+      if (i < n) keys[i] = uint64_t(kv[u][0]) | (uint64_t(kv[u][1]) << 32);
+      if (i + 1 < n) keys[i + 1] = uint64_t(kv[u][2]) | (uint64_t(kv[u][3]) << 32);
+    }
+  }
   if (tid == 0) nsel = 0;
   __syncthreads();
   const uint64_t th = block_select([&](int i) { return keys[i]; }, n, a.K - 1, hist, sc, &res);
