@@ -171,3 +171,32 @@ def test_bf16_tuned_path_largest_k():
     x = synth.make_case("bf16_kmax", case=34, T=300, d=128, V=5000, K=1024,
                         dtype="bf16", tau=1.0, mask_frac=0.05, chunk=128)
     check_case(x)
+
+
+def test_concurrent_calls_on_two_streams():
+    # two calls in flight at once on two streams of the library's runtime,
+    # each with its own workspace and outputs, give the results of the same
+    # calls made one after the other (bitwise)
+    import torch
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+    xa = synth.make_case("conc_a", case=35, T=520, d=192, V=4000, K=40,
+                         dtype="bf16", tau=1.0, mask_frac=0.05, chunk=256)
+    xb = synth.make_case("conc_b", case=36, T=300, d=256, V=3000, K=60,
+                         dtype="bf16", tau=2.0, chunk=128)
+    da, db = G.to_device(xa), G.to_device(xb)
+    ref_a = G.run(da, xa.tau, xa.chunk)
+    ref_b = G.run(db, xb.tau, xb.chunk)
+    sa, sb = hip.Stream(), hip.Stream()
+    out_a = kd.kd_topk_kl_fwd_bwd(da["H"], da["W"], da["topk_idx"], da["topk_logit"],
+                                  da["mask"], xa.tau, xa.chunk, stream=sa.value,
+                                  sync=False)
+    out_b = kd.kd_topk_kl_fwd_bwd(db["H"], db["W"], db["topk_idx"], db["topk_logit"],
+                                  db["mask"], xb.tau, xb.chunk, stream=sb.value,
+                                  sync=False)
+    sa.synchronize()
+    sb.synchronize()
+    torch.cuda.synchronize()
+    for got, want in ((out_a, ref_a), (out_b, ref_b)):
+        for u, v in zip(got, want):
+            assert torch.equal(u, v)
