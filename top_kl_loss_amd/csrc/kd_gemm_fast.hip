@@ -91,21 +91,28 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     __syncthreads();
     const int sr = tid / TPR, part = tid % TPR;
     const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
-    const int cb0 = part * CPT;
-    // base-2 units: v = z / tau * log2(e), P = 2^(v - max v); only the
-    // vocabulary's last segment has columns past V (excluded)
+    // Thread `part` of a row owns the 8-column groups part, part + 8, ...,
+    // so the row's TPR threads store whole 128-byte lines of P together
+    // (contiguous 64-byte runs per thread would split every line).
+    // Base-2 units: v = z / tau * log2(e), P = 2^(v - max v); only the
+    // vocabulary's last segment has columns past V (excluded).
     float v[CPT];
     float mx = -INFINITY;
     const float s2 = a.inv_tau * LOG2E;
     const bool tail = n0 + BN > a.V;
 #pragma unroll
-    for (int c = 0; c < CPT; c += 4) {
-      const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + cb0 + c);
+    for (int j = 0; j < CPT / 8; ++j) {
+      const int col = j * 8 * TPR + part * 8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[c + u] = z[u] * s2;
-        if (tail && n0 + cb0 + c + u >= a.V) v[c + u] = -INFINITY;
-        mx = fmaxf(mx, v[c + u]);
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + col + 4 * h);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = j * 8 + 4 * h + u;
+          v[c] = z[u] * s2;
+          if (tail && n0 + col + 4 * h + u >= a.V) v[c] = -INFINITY;
+          mx = fmaxf(mx, v[c]);
+        }
       }
     }
 #pragma unroll
@@ -122,13 +129,14 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
     if (r < a.C) {
-      uint16_t *dst = P + (size_t)r * a.ldp + n0 + cb0;
+      uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
       if (a.need_grad) {
 #pragma unroll
-        for (int c = 0; c < CPT; c += 8) {
+        for (int j = 0; j < CPT / 8; ++j) {
+          const int c = j * 8;
           u32x4 w{pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]),
                   pack_bf16x2(v[c + 4], v[c + 5]), pack_bf16x2(v[c + 6], v[c + 7])};
-          *reinterpret_cast<u32x4 *>(dst + c) = w;
+          *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) = w;
         }
       }
       if (part == 0) {
