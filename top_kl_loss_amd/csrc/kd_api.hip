@@ -82,8 +82,8 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   // kept only when it is no larger than one slice's G (C >= d), so the extra
   // memory stays bounded by a slice.
   L.wt = L.fast && (int64_t)L.C >= d;
-  L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;
-  L.dh_bn = L.wt ? L.dw_bn : 256;  // the register path of dH is square only
+  L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;  // dW: 192 x 320 tiles when 320
+  L.dh_bn = 256;                                   // dH: 256 x 256 tiles
   L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast, L.dh_bn);
   L.esize = dtype == KD_BF16 ? 2 : 4;
   const size_t C = L.C, nseg = L.nseg;

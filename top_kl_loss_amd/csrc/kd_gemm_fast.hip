@@ -9,8 +9,8 @@
 // G is the slice's logit gradient: k_scale_g writes it in bf16 over the P
 // buffer and also writes G^T; k_transpose_h writes H_c^T.
 //
-// The tile machinery (8-wave 256 x 256 tiles, DMA operand copies, swizzled
-// LDS layout, interleaved MFMA schedule) is in kd_mfma_tile.h.
+// The tile machinery (4-wave and 8-wave tiles, DMA operand copies, swizzled
+// LDS layouts, MFMA schedules) is in kd_mfma_tile.h.
 #include <stdint.h>
 
 #include "kd_device.h"
@@ -24,13 +24,15 @@ namespace {
 using namespace tile;
 
 // ------------------------------------------------------------ logits GEMM
-// A = H_c, B = W (both K-contiguous).  Epilogue per row and segment: max of
-// z/tau, P = exp(z/tau - max) in bf16, the sum of P, and z itself at the
-// row's teacher ids inside the segment (the student-logit gather).
-__global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
+// A = H_c, B = W (both K-contiguous), 4-wave tiles.  Epilogue per row and
+// segment: max of z/tau, P = exp(z/tau - max) in bf16, the sum of P, and z
+// itself at the row's teacher ids inside the segment (the student-logit
+// gather).
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fast_logits(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
   const int nmt = (a.C + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   int mt, seg;
@@ -38,19 +40,21 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
   const int m0 = mt * BM, n0 = seg * SEG;
   const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
   const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  CopyK<8> ca, cb;
+  using S = w4::Square;
+  w4::Copy<S::RA> ca;
+  w4::Copy<S::RB> cb;
   ca.init(H, (uint64_t)a.C * a.d * 2, a.d, m0, wave, lane);
   cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
 
-  // Teacher ids of tile row m0 + tid (tid < 256) inside this segment,
-  // fetched now so that their latency hides under the main loop: up to NHIT
-  // (column, slot) pairs; `more` marks rows with further ids.
+  // Teacher ids of tile row m0 + tid inside this segment, fetched now so
+  // that their latency hides under the main loop: up to NHIT (column, slot)
+  // pairs; `more` marks rows with further ids.
   constexpr int NHIT = 4;
   int hit_col[NHIT], hit_slot[NHIT];
   bool more = false;
 #pragma unroll
   for (int q = 0; q < NHIT; ++q) hit_col[q] = -1;
-  if (tid < BM && m0 + tid < a.C) {
+  if (m0 + tid < a.C) {
     const int r = m0 + tid;
     const int pos = a.first[(size_t)r * a.nseg + seg];
     if (pos >= 0) {
@@ -69,84 +73,107 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
     }
   }
 
-  f32x16 acc[TM][TN];
-  zero_acc(acc);
-  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
-  nt_loop(ca, cb, 0, a.d / BK, lds, ar, br, hh, acc);
+  f32x4 acc[8][8];
+  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
+  w4::acc_ready(acc);
   __syncthreads();
 
-  // Epilogue: one block-row of every wave per pass (64 rows x 256 columns).
+  // Epilogue in 4 passes; pass p stages block-rows 2p and 2p + 1 of both
+  // wave rows: 64 tile rows x 256 columns, tile row
+  // wm * 128 + (2p + ii) * 16 + r at stage row wm * 32 + ii * 16 + r.  Each
+  // row is processed by TPR threads, and each thread takes RPT rows at once
+  // (independent work to overlap with one wave per SIMD).
   constexpr int PITCH = BN + 4;
-  constexpr int SROWS = 64, TPR = NT / SROWS, CPT = BN / TPR;
+  constexpr int SROWS = 64, TPR = 8, RPT = SROWS * TPR / w4::NT, CPT = BN / TPR;
   float *stage = reinterpret_cast<float *>(lds);
   uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
+  const int part = tid % TPR;
+  const float s2 = a.inv_tau * LOG2E;
+  const bool tail = n0 + BN > a.V;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+  for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        stage[(wm * 32 + acc_row(e, lane)) * PITCH + wn * WTN + tn * 32 + (lane & 31)] =
-            acc[tm][tn][e];
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          stage[(wm * 32 + ii * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
+                w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
-    const int sr = tid / TPR, part = tid % TPR;
-    const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
     // Thread `part` of a row owns the 8-column groups part, part + 8, ...,
     // so the row's TPR threads store whole 128-byte lines of P together
     // (contiguous 64-byte runs per thread would split every line).
     // Base-2 units: v = z / tau * log2(e), P = 2^(v - max v); only the
     // vocabulary's last segment has columns past V (excluded).
-    float v[CPT];
-    float mx = -INFINITY;
-    const float s2 = a.inv_tau * LOG2E;
-    const bool tail = n0 + BN > a.V;
+    float v[RPT][CPT];
+    float mx[RPT], sum[RPT];
 #pragma unroll
-    for (int j = 0; j < CPT / 8; ++j) {
-      const int col = j * 8 * TPR + part * 8;
+    for (int q = 0; q < RPT; ++q) {
+      const int sr = tid / TPR + q * (w4::NT / TPR);
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + col + 4 * h);
+      for (int j = 0; j < CPT / 8; ++j) {
+        const int col = j * 8 * TPR + part * 8;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = j * 8 + 4 * h + u;
-          v[c] = z[u] * s2;
-          if (tail && n0 + col + 4 * h + u >= a.V) v[c] = -INFINITY;
-          mx = fmaxf(mx, v[c]);
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + col + 4 * h);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int c = j * 8 + 4 * h + u;
+            v[q][c] = z[u] * s2;
+            if (tail && n0 + col + 4 * h + u >= a.V) v[q][c] = -INFINITY;
+            m4[u] = fmaxf(m4[u], v[q][c]);
+          }
+        }
+      }
+      mx[q] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1)
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        // exp2(-inf) = 0 covers the excluded columns
+        const float pv = __builtin_amdgcn_exp2f(v[q][c] - mx[q]);
+        v[q][c] = pv;
+        s4[c & 3] += pv;
+      }
+      sum[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      mx[q] *= LN2;  // the segment maximum of z / tau
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1)
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) sum[q] += __shfl_xor(sum[q], o, 64);
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      const int sr = tid / TPR + q * (w4::NT / TPR);
+      const int r = m0 + (sr >> 5) * 128 + (2 * pass + ((sr >> 4) & 1)) * 16 + (sr & 15);
+      if (r < a.C) {
+        uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
+        if (a.need_grad) {
+#pragma unroll
+          for (int j = 0; j < CPT / 8; ++j) {
+            const int c = j * 8;
+            u32x4 w{pack_bf16x2(v[q][c], v[q][c + 1]), pack_bf16x2(v[q][c + 2], v[q][c + 3]),
+                    pack_bf16x2(v[q][c + 4], v[q][c + 5]), pack_bf16x2(v[q][c + 6], v[q][c + 7])};
+            *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) = w;
+          }
+        }
+        if (part == 0) {
+          a.mseg[(size_t)r * a.nseg + seg] = mx[q];
+          a.sseg[(size_t)r * a.nseg + seg] = sum[q];
         }
       }
     }
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      // exp2(-inf) = 0 covers the excluded columns
-      const float p = __builtin_amdgcn_exp2f(v[c] - mx);
-      v[c] = p;
-      sum += p;
-    }
-    mx *= LN2;  // the segment maximum of z / tau
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (r < a.C) {
-      uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
-      if (a.need_grad) {
-#pragma unroll
-        for (int j = 0; j < CPT / 8; ++j) {
-          const int c = j * 8;
-          u32x4 w{pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]),
-                  pack_bf16x2(v[c + 4], v[c + 5]), pack_bf16x2(v[c + 6], v[c + 7])};
-          *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) = w;
-        }
-      }
-      if (part == 0) {
-        a.mseg[(size_t)r * a.nseg + seg] = mx;
-        a.sseg[(size_t)r * a.nseg + seg] = sum;
-      }
-    }
-    // Gather z at the teacher ids: thread tid (< 256) owns tile row tid,
-    // staged in this pass when its 32-row block is block-row tm.
-    if (tid < BM && ((tid >> 5) & 3) == tm) {
+    // Gather z at the teacher ids: thread tid owns tile row tid, staged in
+    // pass (tid & 127) >> 5 at stage row (tid >> 7) * 32 + (tid & 31).
+    if (((tid & 127) >> 5) == pass) {
       const int r_own = m0 + tid;
       const int sr_own = (tid >> 7) * 32 + (tid & 31);
       if (r_own < a.C) {
@@ -170,101 +197,131 @@ __global__ __launch_bounds__(NT, 1) void k_fast_logits(SliceArgs a) {
 }
 
 // ---------------------------------------------------------------- dH GEMM
-// A = G (K-contiguous over the vocabulary; copied by DMA).  B = W^T by DMA
-// when the call keeps a W^T copy, else W (vocabulary rows, hidden columns)
-// transposed through registers (square tiles only).
-template <class CF>
-__global__ __launch_bounds__(NT, 1) void k_fast_dh(SliceArgs a) {
+// A = G (K-contiguous over the vocabulary; copied by DMA), B = W
+// (vocabulary rows, hidden contiguous) transposed through registers: the
+// 8-wave path for calls without a W^T copy (slices smaller than d).  With
+// the copy, k_fast_dh4 below runs instead.
+__global__ __launch_bounds__(NT, 1) void k_fast_dh_reg(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / CF::WN, wn = wave % CF::WN;
+  const int wm = wave / WN, wn = wave % WN;
   const int nmt = (a.C + BM - 1) / BM;
-  const int nnt = (a.d + CF::BN - 1) / CF::BN;
+  const int nnt = (a.d + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int split = tile / (nnt * nmt);
   int mt, nt;
   group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * CF::BN;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
   const int kbeg = sbeg * SEG, kend = send * SEG;
   CopyK<8> ca;
   ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-  f32x16 acc[CF::TM][CF::TN];
+  f32x16 acc[TM][TN];
   zero_acc(acc);
   const int nk = (kend - kbeg) / BK;
-  const int ar = wm * CF::WTM + (lane & 31), br = wn * CF::WTN + (lane & 31), hh = lane >> 5;
-  if (a.Wt) {
-    // B = W^T (hidden rows, vocabulary contiguous): both operands by DMA
-    CopyK<8, CF::BN> cb;
-    cb.init(a.Wt, (uint64_t)a.d * a.ldp * 2, a.ldp, n0, wave, lane);
-    nt_loop(ca, cb, kbeg, nk, lds, ar, br, hh, acc);
-  } else if constexpr (CF::BN == BN) {
-    // B = W (vocabulary rows, hidden contiguous) through registers
-    RegMN4 rb;
-    rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
-    ca.issue(lds, kbeg);
-    rb.load(kbeg);
-    rb.store(lds + OP_BYTES, tid);
-    for (int ks = 0; ks < nk; ++ks) {
-      const char *cur = lds + (ks & 1) * STAGE_BYTES;
-      char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-      const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
-      wait_vm0();
-      __syncthreads();
-      ca.issue(nxt, kn);
-      rb.load(kn);
-      kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
-      rb.store(nxt + OP_BYTES, tid);
-    }
+  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
+  RegMN4 rb;
+  rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
+  ca.issue(lds, kbeg);
+  rb.load(kbeg);
+  rb.store(lds + OP_BYTES, tid);
+  for (int ks = 0; ks < nk; ++ks) {
+    const char *cur = lds + (ks & 1) * STAGE_BYTES;
+    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
+    const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
+    wait_vm0();
+    __syncthreads();
+    ca.issue(nxt, kn);
+    rb.load(kn);
+    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
+    rb.store(nxt + OP_BYTES, tid);
   }
   wait_vm0();
 
   float *out = a.dh_part + (size_t)split * a.dh_stride;
 #pragma unroll
-  for (int i = 0; i < CF::TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j) {
-      const int col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * CF::WTM + i * 32 + acc_row(e, lane);
+        const int row = m0 + wm * WTM + i * 32 + acc_row(e, lane);
         if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
       }
     }
 }
 
-// ---------------------------------------------------------------- dW GEMM
-// A = G^T, B = H_c^T (both K-contiguous over the slice's tokens; DMA).
-template <class CF>
-__global__ __launch_bounds__(NT, 1) void k_fast_dw(SliceArgs a) {
+// ---------------------------------------------------------- dH and dW GEMMs
+// On 4-wave tiles, both operands copied by DMA:
+//  dH partials = G (W^T)^T per vocabulary split, A = G, B = W^T (the call's
+//  W^T copy), 256 x 256 tiles;
+//  dW (+)= G^T (H_c^T)^T, A = G^T, B = H_c^T, 192 x 320 tiles when d is a
+//  multiple of 320 (no N padding; d = 2880 = 9 x 320), else 256 x 256.
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fast_dh4(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / CF::WN, wn = wave % CF::WN;
-  const int nnt = (a.d + CF::BN - 1) / CF::BN;
-  const int nmt = (a.V + BM - 1) / BM;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nmt = (a.C + BM - 1) / BM;
+  const int nnt = (a.d + BN - 1) / BN;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int split = tile / (nnt * nmt);
+  int mt, nt;
+  group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
+  const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
+  using S = w4::Square;
+  w4::Copy<S::RA> ca;
+  w4::Copy<S::RB> cb;
+  ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
+  cb.init(a.Wt, (uint64_t)a.d * a.ldp * 2, a.ldp, n0, wave, lane);
+  f32x4 acc[8][8];
+  w4::nt_loop<S>(ca, cb, sbeg * SEG, (send - sbeg) * (SEG / BK), lds, wm, wn, lane, acc);
+  w4::acc_ready(acc);
+  float *out = a.dh_part + (size_t)split * a.dh_stride;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = n0 + wn * 128 + w4::acc_col4(j, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * 128 + w4::acc_row4(i, e, lane);
+        if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
+      }
+    }
+}
+
+template <class S>
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fast_dw4(SliceArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nnt = (a.d + S::RB - 1) / S::RB;
+  const int nmt = (a.V + S::RA - 1) / S::RA;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   int mt, nt;
   group_tile(tile, nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * CF::BN;
-  CopyK<8> ca;
-  CopyK<8, CF::BN> cb;
+  const int m0 = mt * S::RA, n0 = nt * S::RB;
+  w4::Copy<S::RA> ca;
+  w4::Copy<S::RB> cb;
   ca.init(a.Gt, (uint64_t)a.ldp * a.ldh * 2, a.ldh, m0, wave, lane);
   cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave, lane);
-
-  f32x16 acc[CF::TM][CF::TN];
-  zero_acc(acc);
-  const int ar = wm * CF::WTM + (lane & 31), br = wn * CF::WTN + (lane & 31), hh = lane >> 5;
-  nt_loop(ca, cb, 0, (a.C + BK - 1) / BK, lds, ar, br, hh, acc);
-
+  f32x4 acc[S::TMB][S::TNB];
+  w4::nt_loop<S>(ca, cb, 0, (a.C + BK - 1) / BK, lds, wm, wn, lane, acc);
+  w4::acc_ready(acc);
 #pragma unroll
-  for (int i = 0; i < CF::TM; ++i)
+  for (int i = 0; i < S::TMB; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j) {
-      const int col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
+    for (int j = 0; j < S::TNB; ++j) {
+      const int col = n0 + wn * 16 * S::TNB + w4::acc_col4(j, lane);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * CF::WTM + i * 32 + acc_row(e, lane);
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * 16 * S::TMB + w4::acc_row4(i, e, lane);
         if (row < a.V && col < a.d) {
           float *p = a.dW + (size_t)row * a.d + col;
           // exactly one addition per element and slice, slices in stream
@@ -351,12 +408,13 @@ __global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
 }
 
 template <typename K>
-hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds = LDS_BYTES) {
+hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds = LDS_BYTES,
+                  int threads = NT) {
   if (grid <= 0) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -390,15 +448,14 @@ int fast_dh_splits(int C, int d, int nseg, int bn) {
 }
 
 hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
-  return launch(k_fast_logits, ((a.C + BM - 1) / BM) * a.nseg, a, s);
+  if (a.d < BK) return hipErrorInvalidValue;  // the main loop needs one k-step
+  return launch(k_fast_logits, ((a.C + BM - 1) / BM) * a.nseg, a, s, w4::Square::LDS, w4::NT);
 }
 
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
-  const int nmt = (a.C + BM - 1) / BM;
-  if (a.dh_bn == WideCfg::BN)
-    return launch(k_fast_dh<WideCfg>, nmt * ((a.d + WideCfg::BN - 1) / WideCfg::BN) * a.splits,
-                  a, s, WideCfg::LDS);
-  return launch(k_fast_dh<SquareCfg>, nmt * ((a.d + BN - 1) / BN) * a.splits, a, s);
+  const int tiles = ((a.C + BM - 1) / BM) * ((a.d + BN - 1) / BN) * a.splits;
+  if (a.Wt) return launch(k_fast_dh4, tiles, a, s, w4::Square::LDS, w4::NT);
+  return launch(k_fast_dh_reg, tiles, a, s);
 }
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
@@ -423,11 +480,14 @@ hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
-  const int nmt = (a.V + BM - 1) / BM;
-  if (a.dw_bn == WideCfg::BN)
-    return launch(k_fast_dw<WideCfg>, nmt * ((a.d + WideCfg::BN - 1) / WideCfg::BN), a, s,
-                  WideCfg::LDS);
-  return launch(k_fast_dw<SquareCfg>, nmt * ((a.d + BN - 1) / BN), a, s);
+  if (a.dw_bn == w4::Tall::RB) {
+    using S = w4::Tall;
+    return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
+                  S::LDS, w4::NT);
+  }
+  using S = w4::Square;
+  return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
+                S::LDS, w4::NT);
 }
 
 }  // namespace kd

@@ -1,18 +1,23 @@
 // Matrix-core tile machinery shared by the tuned bf16 GEMMs (gfx950).
 //
-// Workgroup: 512 threads = 8 waves (2 per SIMD) as 2 (M) x 4 (N); tile
-// 256 x 256, wave tile 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators.  Two waves per SIMD let the hardware interleave
-// one wave's LDS/VMEM/VALU work with the other's MFMAs.  One k-step is 64
-// bf16 of the contraction, double-buffered in LDS (2 x 64 KiB).
+// Two families.  The 4-wave tiles (namespace w4, below) run the logits,
+// dH and dW products: one wave per SIMD, 128 x 128 (or 96 x 160) wave tiles
+// of v_mfma_f32_16x16x32_bf16 with the accumulators in AGPRs.  On this chip
+// the GEMMs run power-limited (the shader clock drops under MFMA load), and
+// these tiles read fewer LDS bytes per flop and keep the matrix cores busier
+// per clock than the 8-wave ones.  The 8-wave tiles (512 threads, 2 waves
+// per SIMD as 2 (M) x 4 (N), 256 x 256 tile, wave tile 128 x 64 = 4 x 2
+// blocks of v_mfma_f32_32x32x16_bf16) remain for the operands that go
+// through registers (dH without a W^T copy; the teacher builder), where the
+// second wave per SIMD hides the register-path work.
 //
 // Every operand tile sits in LDS as rows of 64 contraction elements (128
-// bytes), 16-byte chunk c of row r at r*128 + ((c ^ swz(r)) * 16) with
-// swz(r) = (r ^ (r >> 3)) & 7, and MFMA fragments are read with
-// ds_read_b128.  Operands whose contraction index is contiguous in memory are
-// copied HBM -> LDS with buffer_load_dwordx4 ... lds (reads past the buffer
-// end return zero); the others are read as 8 x 4 bf16 blocks into registers,
-// transposed with v_perm_b32 and written with ds_write_b128.
+// bytes), 16-byte chunk c of row r at r*128 + ((c ^ swz(r)) * 16), and MFMA
+// fragments are read with ds_read_b128.  Operands whose contraction index is
+// contiguous in memory are copied HBM -> LDS with buffer_load_dwordx4 ... lds
+// (reads past the buffer end return zero); the others are read as 8 x 4
+// bf16 blocks into registers, transposed with v_perm_b32 and written with
+// ds_write_b128.
 #pragma once
 
 #include <stdint.h>
@@ -29,10 +34,8 @@ constexpr int OP_BYTES = 256 * 128;          // one operand tile per stage
 constexpr int STAGE_BYTES = 2 * OP_BYTES;    // A then B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // 128 KiB
 
-// Tile shapes with 256 rows of A: 8 waves as (8/WN_) x WN_, each wave
-// TM_ x TN_ blocks of 32 x 32.  Square: 256 x 256 (the default above);
-// Wide: 256 x 320 for N = d multiple of 320 (d = 2880 = 9 x 320 wastes no
-// MFMA work on padding, where 256-wide tiles waste 6.25%).
+// Tile shape of the 8-wave kernels: 8 waves as (8/WN_) x WN_, each wave
+// TM_ x TN_ blocks of 32 x 32 (256 x 256 with the defaults above).
 template <int WN_, int TM_, int TN_>
 struct TileCfg {
   static constexpr int WN = WN_, TM = TM_, TN = TN_;
@@ -42,10 +45,9 @@ struct TileCfg {
   static_assert((8 / WN_) * WTM == 256, "256 rows of A");
 };
 using SquareCfg = TileCfg<4, 4, 2>;
-using WideCfg = TileCfg<2, 2, 5>;
-static_assert(WideCfg::BN == 320 && WideCfg::LDS <= 160 * 1024, "wide tile");
 
-// Width of the N tile that wastes the least MFMA work on a dimension of n.
+// Width (256 or 320) of the N tile that wastes the least MFMA work on a
+// dimension of n (d = 2880 = 9 x 320 needs no padding at 320).
 inline int best_bn(int n) {
   const int w256 = (n + 255) / 256 * 256 - n, w320 = (n + 319) / 320 * 320 - n;
   return w320 < w256 ? 320 : 256;
@@ -253,6 +255,209 @@ __device__ __forceinline__ void nt_loop(CopyK<8, RA> &ca, CopyK<8, RB> &cb, int 
   }
   wait_vm0();
 }
+
+
+// ------------------------------------------------------------ 4-wave tiles
+// Workgroup: 256 threads = 4 waves (one per SIMD) as 2 (M) x 2 (N); tile
+// 256 x 256, wave tile 128 x 128 = 8 x 8 blocks of v_mfma_f32_16x16x32_bf16
+// with the 256 accumulator registers in AGPRs.  A k-step (64) is two k32
+// halves.  Fragments are double-buffered in registers: while one half's 64
+// MFMAs run, the other half's 16 fragments are read from LDS (in the order
+// the MFMAs use them).  The one barrier per k-step sits between the halves,
+// so the MFMAs right after it use fragments already in registers; the copy
+// of step ks + 2 is issued during the second half into the stage just
+// consumed, which leaves it a whole k-step to land.  Fewer LDS bytes per
+// flop than the 8-wave layout, and one wave per SIMD, keep the matrix cores
+// busier per joule: the GEMMs here run power-limited.
+//
+// The MFMAs are inline asm with the accumulator tied ("+a"), which keeps the
+// compiler from copying accumulators between AGPRs and keeps the source
+// order.  The compiler's hazard checks do not see asm: the first MFMA of
+// every accumulator takes srcC = 0 (no VALU zeroing), and acc_ready() pads
+// with s_nop before the accumulators are read.  LDS layout as above, with
+// swz4(row) = (row & 7) ^ ((row >> 3) & 1), which is the same for rows 16
+// apart, so a fragment address is one register plus an immediate.
+namespace w4 {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ int swz4(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Tile of 2 x 2 waves, each TMB x TNB blocks of 16 x 16: A has 32 TMB rows,
+// B 32 TNB rows per stage (128 bytes each).  Every half-step reads
+// TMB + TNB = 16 fragments and issues 16 copy instructions per wave.
+template <int TMB_, int TNB_>
+struct Shape {
+  static constexpr int TMB = TMB_, TNB = TNB_;
+  static constexpr int RA = 32 * TMB, RB = 32 * TNB;  // operand rows per stage
+  static constexpr int OPA = RA * 128;                // B starts here
+  static constexpr int STB = (RA + RB) * 128;
+  static constexpr int LDS = 2 * STB;
+  static constexpr int NR = TMB + TNB;
+  static_assert(NR == 16, "16 fragment reads and copy instructions per half-step");
+  static_assert(TMB * TNB * 4 <= 256, "accumulators fit the AGPRs");
+};
+using Square = Shape<8, 8>;   // 256 x 256
+using Tall = Shape<6, 10>;    // 192 x 320 (N = d multiple of 320)
+static_assert(Tall::LDS <= 160 * 1024, "LDS");
+
+// ROWS rows of a K-contiguous operand, element (mn, k) at byte
+// (mn * ld + k) * 2 of `res`; wave w issues ROWS / 32 instructions of 1 KiB.
+template <int ROWS>
+struct Copy {
+  static constexpr int N = ROWS / 32;
+  __amdgpu_buffer_rsrc_t res;
+  uint32_t off[N];
+  int w;
+  __device__ __forceinline__ void init(const void *base, uint64_t bytes, int64_t ld, int mn0,
+                                       int w_, int lane) {
+    res = make_res(base, bytes);
+    w = w_;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int p = (w * N + n) * 64 + lane;
+      const int row = p >> 3, pc = p & 7;
+      off[n] = (uint32_t)(((int64_t)(mn0 + row) * ld + (pc ^ swz4(row)) * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(char *tile, int k0, int n) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_vptr)(tile + (w * N + n) * 1024), 16,
+                                             (int)(off[n] + k0 * 2), 0, 0, 0);
+  }
+  __device__ __forceinline__ void issue_all(char *tile, int k0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) issue(tile, k0, n);
+  }
+};
+
+__device__ __forceinline__ void mfma(f32x4 &acc, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_first(f32x4 &acc, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+
+// Byte offsets (within a stage) of this lane's fragments of block 0:
+// A rows wm * 16 TMB + (lane & 15), B rows wn * 16 TNB + (lane & 15),
+// k-half h chunk 4 h + (lane >> 4); block i adds i * 2048.
+template <class S>
+struct FragOff {
+  int a[2], b[2];
+  __device__ __forceinline__ FragOff(int wm, int wn, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = ((4 * h + kq) ^ swz4(r)) << 4;
+      a[h] = (wm * 16 * S::TMB + r) * 128 + c;
+      b[h] = S::OPA + (wn * 16 * S::TNB + r) * 128 + c;
+    }
+  }
+};
+
+__device__ __forceinline__ u32x4 rd(const char *stage, int off, int i) {
+  return *reinterpret_cast<const u32x4 *>(stage + off + i * 2048);
+}
+
+// Fragment r of a half in the order the MFMAs use them: A0, B0.., A1...
+template <class S>
+__device__ __forceinline__ void read_frag(const char *stage, int aoff, int boff, int r,
+                                          u32x4 (&fa)[S::TMB], u32x4 (&fb)[S::TNB]) {
+  if (r == 0)
+    fa[0] = rd(stage, aoff, 0);
+  else if (r <= S::TNB)
+    fb[r - 1] = rd(stage, boff, r - 1);
+  else
+    fa[r - S::TNB] = rd(stage, aoff, r - S::TNB);
+}
+
+// The TMB x TNB MFMAs of one k32 half on (fa, fb), spread over 16 slots; in
+// slot r, fragment r of the next half is read (and, when CP, copy
+// instruction r of the next-but-one k-step is issued).
+template <class S, bool FIRST, bool CP>
+__device__ __forceinline__ void half_step(f32x4 (&acc)[S::TMB][S::TNB],
+                                          const u32x4 (&fa)[S::TMB], const u32x4 (&fb)[S::TNB],
+                                          const char *rstage, int aoff, int boff,
+                                          u32x4 (&na)[S::TMB], u32x4 (&nb)[S::TNB],
+                                          Copy<S::RA> &ca, Copy<S::RB> &cb, char *cstage, int kc) {
+  constexpr int NM = S::TMB * S::TNB;
+#pragma unroll
+  for (int r = 0; r < S::NR; ++r) {
+    read_frag<S>(rstage, aoff, boff, r, na, nb);
+    if (CP) {
+      if (r < Copy<S::RA>::N)
+        ca.issue(cstage, kc, r);
+      else
+        cb.issue(cstage + S::OPA, kc, r - Copy<S::RA>::N);
+    }
+#pragma unroll
+    for (int idx = r * NM / S::NR; idx < (r + 1) * NM / S::NR; ++idx) {
+      const int i = idx / S::TNB, j = idx % S::TNB;
+      if (FIRST)
+        mfma_first(acc[i][j], fa[i], fb[j]);
+      else
+        mfma(acc[i][j], fa[i], fb[j]);
+    }
+  }
+}
+
+// NT main loop: acc = A[m0.., kbeg + 64 nk) B[n0.., ...)^T, both operands
+// K-contiguous and copied by DMA; nk >= 1.  On return every copy has
+// landed; callers reusing LDS call __syncthreads first.
+template <class S>
+__device__ __forceinline__ void nt_loop(Copy<S::RA> &ca, Copy<S::RB> &cb, int kbeg, int nk,
+                                        char *lds, int wm, int wn, int lane,
+                                        f32x4 (&acc)[S::TMB][S::TNB]) {
+  const FragOff<S> fo(wm, wn, lane);
+  u32x4 fa0[S::TMB], fb0[S::TNB], fa1[S::TMB], fb1[S::TNB];
+  ca.issue_all(lds, kbeg);
+  cb.issue_all(lds + S::OPA, kbeg);
+  wait_vm0();
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < S::NR; ++r) read_frag<S>(lds, fo.a[0], fo.b[0], r, fa0, fb0);
+  const int k1 = kbeg + (nk > 1 ? 1 : 0) * BK;
+  ca.issue_all(lds + S::STB, k1);
+  cb.issue_all(lds + S::STB + S::OPA, k1);
+  // k-step 0: the first half sets every accumulator (srcC = 0)
+  {
+    half_step<S, true, false>(acc, fa0, fb0, lds, fo.a[1], fo.b[1], fa1, fb1, ca, cb, lds, 0);
+    wait_vm0();
+    __syncthreads();
+    const int k2 = kbeg + (nk > 2 ? 2 : nk - 1) * BK;
+    half_step<S, false, true>(acc, fa1, fb1, lds + S::STB, fo.a[0], fo.b[0], fa0, fb0, ca, cb,
+                              lds, k2);
+  }
+  for (int ks = 1; ks < nk; ++ks) {
+    char *cur = lds + (ks & 1) * S::STB;
+    char *nxt = lds + ((ks + 1) & 1) * S::STB;
+    half_step<S, false, false>(acc, fa0, fb0, cur, fo.a[1], fo.b[1], fa1, fb1, ca, cb, cur, 0);
+    // this stage is fully read and the copy of step ks + 1 has landed
+    wait_vm0();
+    __syncthreads();
+    // the last step re-copies its own k-slice into the idle stage (never read)
+    const int k2 = kbeg + (ks + 2 < nk ? ks + 2 : nk - 1) * BK;
+    half_step<S, false, true>(acc, fa1, fb1, nxt, fo.a[0], fo.b[0], fa0, fb0, ca, cb, cur, k2);
+  }
+  wait_vm0();
+}
+
+// Wait states between the last MFMA and the first read of its accumulator
+// (the hazard check does not see the asm MFMAs); the empty asm statements
+// order every accumulator read after the padding.
+template <int TMB, int TNB>
+__device__ __forceinline__ void acc_ready(f32x4 (&acc)[TMB][TNB]) {
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < TMB; ++i)
+#pragma unroll
+    for (int j = 0; j < TNB; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// Position of accumulator element e of block (i, j) in the wave tile.
+__device__ __forceinline__ int acc_row4(int i, int e, int lane) { return i * 16 + 4 * (lane >> 4) + e; }
+__device__ __forceinline__ int acc_col4(int j, int lane) { return j * 16 + (lane & 15); }
+
+}  // namespace w4
 
 }  // namespace tile
 }  // namespace kd
