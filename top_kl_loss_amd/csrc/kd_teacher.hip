@@ -54,15 +54,16 @@ __device__ __forceinline__ void write_row(const TkArgs &a, int64_t t, const uint
 // ------------------------------------------------------------ the GEMM
 constexpr int SAMPLE = 0, FILTER = 1;
 
-// Tile (mt, segment) of z = H_c W^T on the tuned bf16 main loop.  SAMPLE:
-// the tile columns are sampled segment nt, stored to zs.  FILTER: every
-// non-sampled segment; entries with key <= the row's threshold are
+// Tile (mt, segment) of z = H_c W^T on the 4-wave bf16 main loop.
+// SAMPLE: the tile columns are sampled segment nt, stored to zs.  FILTER:
+// every non-sampled segment; entries with key <= the row's threshold are
 // appended to the row's candidates.
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void k_tk_gemm(TkArgs a) {
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_tk_gemm(TkArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
   const int nmt = (a.C + BM - 1) / BM;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   int mt, nt;
@@ -72,91 +73,102 @@ __global__ __launch_bounds__(NT, 1) void k_tk_gemm(TkArgs a) {
   const int m0 = mt * BM, n0 = seg * SEG;
   const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
   const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  CopyK<8> ca, cb;
+  using S = w4::Square;
+  w4::Copy<S::RA> ca;
+  w4::Copy<S::RB> cb;
   ca.init(H, (uint64_t)a.C * a.d * 2, a.d, m0, wave, lane);
   cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
 
-  // Epilogue layout (as the loss's logits GEMM): one block-row of every
-  // wave per pass, 64 rows x 256 columns, 8 threads per row.
+  // Epilogue layout (as the loss's logits GEMM): 4 passes of 64 tile rows
+  // (block-rows 2p, 2p + 1 of both wave rows), 8 threads per row with 32
+  // contiguous columns each, 2 rows per thread.
   constexpr int PITCH = BN + 4;
-  constexpr int SROWS = 64, TPR = NT / SROWS, CPT = BN / TPR;
-  const int sr = tid / TPR, part = tid % TPR;
-  float th_v[TM];
-  int th_i[TM];
-  if (MODE == FILTER) {
-    // thresholds of this thread's rows, fetched under the main loop
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
-      th_v[tm] = r < a.C ? a.th_v[r] : INFINITY;
-      th_i[tm] = r < a.C ? a.th_i[r] : -1;
-    }
-  }
-
-  f32x16 acc[TM][TN];
-  zero_acc(acc);
-  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
-  nt_loop(ca, cb, 0, a.d / BK, lds, ar, br, hh, acc);
+  constexpr int TPR = 8, RPT = 2, CPT = BN / TPR;
+  const int part = tid % TPR;
+  auto row_of = [&](int pass, int q) {
+    const int sr = tid / TPR + q * (w4::NT / TPR);
+    return m0 + (sr >> 5) * 128 + (2 * pass + ((sr >> 4) & 1)) * 16 + (sr & 15);
+  };
+  f32x4 acc[8][8];
+  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
+  w4::acc_ready(acc);
   __syncthreads();
 
   float *stage = reinterpret_cast<float *>(lds);
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+  for (int pass = 0; pass < 4; ++pass) {
+    // thresholds of this pass's rows (their latency overlaps the staging)
+    float th_v[RPT];
+    int th_i[RPT];
+    if (MODE == FILTER) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+      for (int q = 0; q < RPT; ++q) {
+        const int r = row_of(pass, q);
+        th_v[q] = r < a.C ? a.th_v[r] : INFINITY;
+        th_i[q] = r < a.C ? a.th_i[r] : -1;
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        stage[(wm * 32 + acc_row(e, lane)) * PITCH + wn * WTN + tn * 32 + (lane & 31)] =
-            acc[tm][tn][e];
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          stage[(wm * 32 + ii * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
+                w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
-    const int r = m0 + (sr >> 5) * WTM + tm * 32 + (sr & 31);
     const int cb0 = part * CPT;
-    const float *srow = stage + sr * PITCH + cb0;
-    if (MODE == SAMPLE) {
-      if (r < a.C) {
-        float *dst = a.zs + (size_t)r * a.ldzs + nt * SEG + cb0;
 #pragma unroll
-        for (int c = 0; c < CPT; c += 4)
-          *reinterpret_cast<f32x4 *>(dst + c) = *reinterpret_cast<const f32x4 *>(srow + c);
-      }
-    } else {
-      const float tv = th_v[tm];
-      const int ti = th_i[tm];
-      uint32_t m = 0u;
+    for (int q = 0; q < RPT; ++q) {
+      const int sr = tid / TPR + q * (w4::NT / TPR);
+      const int r = row_of(pass, q);
+      const float *srow = stage + sr * PITCH + cb0;
+      if (MODE == SAMPLE) {
+        if (r < a.C) {
+          float *dst = a.zs + (size_t)r * a.ldzs + nt * SEG + cb0;
 #pragma unroll
-      for (int c = 0; c < CPT; c += 4) {
-        const f32x4 z = *reinterpret_cast<const f32x4 *>(srow + c);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int id = n0 + cb0 + c + u;
-          const bool hit = z[u] > tv || (z[u] == tv && id <= ti);
-          m |= uint32_t(hit) << (c + u);
+          for (int c = 0; c < CPT; c += 4)
+            *reinterpret_cast<f32x4 *>(dst + c) = *reinterpret_cast<const f32x4 *>(srow + c);
         }
-      }
-      const int lim = a.V - (n0 + cb0);  // columns of this thread below V
-      if (lim < CPT) m = lim <= 0 ? 0u : (m & ((1u << lim) - 1u));
-      const int n = __popc(m);
-      int incl = n;
+      } else {
+        const float tv = th_v[q];
+        const int ti = th_i[q];
+        uint32_t m = 0u;
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) {
-        const int y = __shfl_up(incl, o, TPR);
-        if (part >= o) incl += y;
-      }
-      const int total = __shfl(incl, TPR - 1, TPR);
-      int base = 0;
-      if (part == TPR - 1 && total > 0 && r < a.C) base = atomicAdd(a.cnt + r, total);
-      base = __shfl(base, TPR - 1, TPR);
-      if (m != 0u && r < a.C) {
-        int pos = base + incl - n;
-        uint64_t *dst = a.cand + (size_t)r * a.cap;
-        while (m != 0u) {
-          const int i = __builtin_ctz(m);
-          m &= m - 1u;
-          if (pos < a.cap) dst[pos] = make_key(srow[i], n0 + cb0 + i);
-          ++pos;
+        for (int c = 0; c < CPT; c += 4) {
+          const f32x4 z = *reinterpret_cast<const f32x4 *>(srow + c);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int id = n0 + cb0 + c + u;
+            const bool hit = z[u] > tv || (z[u] == tv && id <= ti);
+            m |= uint32_t(hit) << (c + u);
+          }
         }
+        const int lim = a.V - (n0 + cb0);  // columns of this thread below V
+        if (lim < CPT) m = lim <= 0 ? 0u : (m & ((1u << lim) - 1u));
+        const int n = __popc(m);
+        int incl = n;
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) {
+          const int y = __shfl_up(incl, o, TPR);
+          if (part >= o) incl += y;
+        }
+        const int total = __shfl(incl, TPR - 1, TPR);
+        int base = 0;
+        if (part == TPR - 1 && total > 0 && r < a.C) base = atomicAdd(a.cnt + r, total);
+        base = __shfl(base, TPR - 1, TPR);
+        if (m != 0u && r < a.C) {
+          int pos = base + incl - n;
+          uint64_t *dst = a.cand + (size_t)r * a.cap;
+          while (m != 0u) {
+            const int i = __builtin_ctz(m);
+            m &= m - 1u;
+            if (pos < a.cap) dst[pos] = make_key(srow[i], n0 + cb0 + i);
+            ++pos;
+          }
+        }
+        if (part == TPR - 1 && r < a.C && total > 0 && base + total > a.cap) a.ovf[r] = 1;
       }
-      if (part == TPR - 1 && r < a.C && total > 0 && base + total > a.cap) a.ovf[r] = 1;
     }
     __syncthreads();
   }
@@ -328,7 +340,7 @@ hipError_t launch_dyn(K kern, int grid, int threads, int lds_bytes, const TkArgs
 }  // namespace
 
 hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s) {
-  return launch_dyn(k_tk_gemm<SAMPLE>, ((a.C + BM - 1) / BM) * a.ns, NT, LDS_BYTES, a, s);
+  return launch_dyn(k_tk_gemm<SAMPLE>, ((a.C + BM - 1) / BM) * a.ns, w4::NT, w4::Square::LDS, a, s);
 }
 
 hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s) {
@@ -339,7 +351,7 @@ hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s) {
 
 hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s) {
   if (a.ns == a.nseg) return hipSuccess;  // every segment was sampled
-  return launch_dyn(k_tk_gemm<FILTER>, ((a.C + BM - 1) / BM) * a.nseg, NT, LDS_BYTES, a, s);
+  return launch_dyn(k_tk_gemm<FILTER>, ((a.C + BM - 1) / BM) * a.nseg, w4::NT, w4::Square::LDS, a, s);
 }
 
 hipError_t launch_tk_select(const TkArgs &a, hipStream_t s) {
