@@ -7,9 +7,9 @@
 // these tiles read fewer LDS bytes per flop and keep the matrix cores busier
 // per clock than the 8-wave ones.  The 8-wave tiles (512 threads, 2 waves
 // per SIMD as 2 (M) x 4 (N), 256 x 256 tile, wave tile 128 x 64 = 4 x 2
-// blocks of v_mfma_f32_32x32x16_bf16) remain for the operands that go
-// through registers (dH without a W^T copy; the teacher builder), where the
-// second wave per SIMD hides the register-path work.
+// blocks of v_mfma_f32_32x32x16_bf16) remain for dH without a W^T copy
+// (slices smaller than d), whose W operand goes through registers: there
+// the second wave per SIMD hides the register-path work.
 //
 // Every operand tile sits in LDS as rows of 64 contraction elements (128
 // bytes), 16-byte chunk c of row r at r*128 + ((c ^ swz(r)) * 16), and MFMA
