@@ -127,8 +127,9 @@ def test_repeat_is_bitwise_identical_and_accumulate_adds():
 
 def test_bf16_tuned_path_ragged_tails():
     # d a multiple of 64 (tuned kernels) but not of the 256-wide tiles, V not
-    # a multiple of the segment, chunk not a multiple of the 256-row tile,
-    # T not a multiple of chunk, padding rows, tau != 1.
+    # a multiple of the segment, chunk not a multiple of the 256-row tile nor
+    # of the 64-token k-step of dW, chunk < d (dH transposes W through
+    # registers), T not a multiple of chunk, padding rows, tau != 1.
     x = synth.make_case("bf16_tuned_ragged", case=30, T=700, d=320, V=3001,
                         K=37, dtype="bf16", tau=1.3, mask_frac=0.1, chunk=300)
     check_case(x)
@@ -159,8 +160,9 @@ def test_bf16_tuned_path_with_transposed_weight_copy():
 
 
 def test_bf16_tuned_path_wide_tiles_with_transposed_weight_copy():
-    # d a multiple of 320: the dH and dW GEMMs use 256 x 320 tiles (dH with
-    # the W^T copy since chunk >= d); ragged T, V, padding rows
+    # d a multiple of 320: dW runs on 192 x 320 tiles, dH on 256 x 256 tiles
+    # with a ragged N tile (W^T copy since chunk >= d); ragged T, V (192-row
+    # tiles), padding rows
     x = synth.make_case("bf16_wide", case=33, T=900, d=640, V=3001, K=64,
                         dtype="bf16", tau=1.2, mask_frac=0.05, chunk=640)
     check_case(x)
