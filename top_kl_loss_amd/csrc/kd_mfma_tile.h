@@ -34,18 +34,6 @@ constexpr int OP_BYTES = 256 * 128;          // one operand tile per stage
 constexpr int STAGE_BYTES = 2 * OP_BYTES;    // A then B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // 128 KiB
 
-// Tile shape of the 8-wave kernels: 8 waves as (8/WN_) x WN_, each wave
-// TM_ x TN_ blocks of 32 x 32 (256 x 256 with the defaults above).
-template <int WN_, int TM_, int TN_>
-struct TileCfg {
-  static constexpr int WN = WN_, TM = TM_, TN = TN_;
-  static constexpr int WTM = TM_ * 32, WTN = TN_ * 32;
-  static constexpr int BN = WN_ * WTN;
-  static constexpr int LDS = 2 * (256 + BN) * 128;
-  static_assert((8 / WN_) * WTM == 256, "256 rows of A");
-};
-using SquareCfg = TileCfg<4, 4, 2>;
-
 // Width (256 or 320) of the N tile that wastes the least MFMA work on a
 // dimension of n (d = 2880 = 9 x 320 needs no padding at 320).
 inline int best_bn(int n) {
@@ -230,32 +218,6 @@ __device__ __forceinline__ void group_tile(int L, int nm, int nn, int gm_max, in
   m = first + r % gm;
   n = r / gm;
 }
-
-// Main loop of an NT product (both operands K-contiguous, copied by DMA):
-// nk k-steps starting at contraction index kbeg.
-// nk k-steps starting at contraction index kbeg; a stage holds RA rows of A
-// then RB rows of B (128 bytes each).
-template <int RA, int RB, int TM_, int TN_>
-__device__ __forceinline__ void nt_loop(CopyK<8, RA> &ca, CopyK<8, RB> &cb, int kbeg, int nk,
-                                        char *lds, int ar, int br, int hh,
-                                        f32x16 (&acc)[TM_][TN_]) {
-  constexpr int OPA = RA * 128, ST = (RA + RB) * 128;
-  ca.issue(lds, kbeg);
-  cb.issue(lds + OPA, kbeg);
-  for (int ks = 0; ks < nk; ++ks) {
-    const char *cur = lds + (ks & 1) * ST;
-    char *nxt = lds + ((ks + 1) & 1) * ST;
-    // the last step re-copies itself into the idle stage (never read)
-    const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
-    wait_vm0();
-    __syncthreads();
-    ca.issue(nxt, kn);
-    cb.issue(nxt + OPA, kn);
-    kstep(cur, cur + OPA, ar, br, hh, acc);
-  }
-  wait_vm0();
-}
-
 
 // ------------------------------------------------------------ 4-wave tiles
 // Workgroup: 256 threads = 4 waves (one per SIMD) as 2 (M) x 2 (N); tile
