@@ -335,41 +335,47 @@ void k_fast_dw4(SliceArgs a) {
     }
 }
 
-// Ht[j, t] = H[c0 + t, j] for t < C, 0 for C <= t < ldh (bf16), through
-// 64 x 64 tiles in LDS.
-__global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
+// dst[j * ldd + r] = src[r * d + j] for r < nrows, 0 for nrows <= r < ldd
+// (bf16, d and ldd multiples of 64), over 64 (r) x 64 (j) tiles: 16-byte
+// loads of the source rows, a transposing read from LDS, 16-byte stores of
+// the destination rows.  256 threads.
+__device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, int64_t d, int nrows,
+                                            uint16_t *__restrict__ dst, int64_t ldd) {
+  // pitch 66 elements: the column reads of 8 rows 8 apart hit 8 banks
   __shared__ uint16_t t_s[64][66];
-  const int t0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-  const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, c = i & 63;
-    const int t = t0 + r, j = j0 + c;
-    t_s[r][c] = (t < a.C && j < a.d) ? H[(size_t)t * a.d + j] : uint16_t(0);
+  const int r0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, ch = tid & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = (tid >> 3) + 32 * h;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (r0 + rr < nrows) v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + rr) * d + j0 + ch * 8);
+    uint32_t *row = reinterpret_cast<uint32_t *>(&t_s[rr][0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) row[ch * 4 + q] = v[q];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, c = i & 63;  // r: hidden index, c: token
-    const int j = j0 + r, t = t0 + c;
-    if (j < a.d && t < a.ldh) a.Ht[(size_t)j * a.ldh + t] = t_s[c][r];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jj = (tid >> 3) + 32 * h;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ra = ch * 8 + 2 * q;
+      o[q] = uint32_t(t_s[ra][jj]) | (uint32_t(t_s[ra + 1][jj]) << 16);
+    }
+    *reinterpret_cast<u32x4 *>(dst + (int64_t)(j0 + jj) * ldd + r0 + ch * 8) = o;
   }
 }
 
-// Wt[j, v] = W[v, j] for v < V, 0 for V <= v < ldp, through 64 x 64 tiles.
+// H_c^T [d, ldh] per slice (token columns t >= C zero).
+__global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
+  transpose64(reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d, a.d, a.C, a.Ht, a.ldh);
+}
+
+// W^T [d, ldp] once per call (vocabulary columns v >= V zero).
 __global__ __launch_bounds__(256) void k_transpose_w(SliceArgs a) {
-  __shared__ uint16_t t_s[64][66];
-  const int v0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-  const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, c = i & 63;
-    const int v = v0 + r, j = j0 + c;
-    t_s[r][c] = (v < a.V && j < a.d) ? W[(size_t)v * a.d + j] : uint16_t(0);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, c = i & 63;  // r: hidden index, c: vocabulary
-    const int j = j0 + r, v = v0 + c;
-    if (j < a.d && v < a.ldp) a.Wt[(size_t)j * a.ldp + v] = t_s[c][r];
-  }
+  transpose64(reinterpret_cast<const uint16_t *>(a.W), a.d, a.V, a.Wt, a.ldp);
 }
 
 // G = f[t, seg] * P over one 64-row x 256-column (one segment) tile, written
@@ -460,14 +466,14 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
-  const dim3 tg((a.ldh + 63) / 64, (a.d + 63) / 64);
+  const dim3 tg(a.ldh / 64, a.d / 64);
   hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s) {
   if (!a.Wt) return hipSuccess;
-  const dim3 g(a.ldp / 64, (a.d + 63) / 64);
+  const dim3 g(a.ldp / 64, a.d / 64);
   hipLaunchKernelGGL(k_transpose_w, g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
