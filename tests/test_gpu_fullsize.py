@@ -123,6 +123,32 @@ def test_t32k_bench_configuration():
     _check_identities(x, dev, dH, dW)
 
 
+def test_t32k_slices_past_4_gib_buffers():
+    # chunk 16384: the slice's probability / gradient buffer (16384 x 201216
+    # bf16 = 6.6 GB) and its transpose exceed the 4 GiB reach of 32-bit
+    # buffer offsets; the tiles address them from their own first row.
+    # Rows are independent, so the row losses and the loss equal those of the
+    # benchmark's slice size bit for bit (which also shows that the tuned
+    # kernels ran: the generic ones round differently); the gradients differ
+    # only in the order of fp32 partial sums.
+    import torch
+    x = synth.workload("t32k", teacher_device="cuda")
+    dev = G.to_device(x)
+    _say(f"t32k: chunk={x.chunk}")
+    loss_a, rl_a, dH_a, dW_a = G.run(dev, x.tau, x.chunk)
+    _say("t32k: chunk=16384")
+    loss_b, rl_b, dH_b, dW_b = G.run(dev, x.tau, 16384)
+    assert torch.equal(rl_a, rl_b)
+    assert float(loss_a.item()) == float(loss_b.item())
+    for name, g, o in (("dH", dH_b, dH_a), ("dW", dW_b, dW_a)):
+        err = float((g - o).abs().max()) / float(o.abs().max())
+        assert err <= 1e-5, f"chunk 16384: {name} differs by {err:.2e}"
+    rows = _sample_rows(x, extra=(16383, 16384, 32767))
+    _check_rows(x, rl_b, dH_b, rows)
+    del loss_a, rl_a, dH_a, dW_a
+    torch.cuda.empty_cache()
+
+
 def test_t32k_d4096_chunk_sweep():
     # d = 4096, V = 151936, tau = 2, 15% padding; slice sizes 512 ... 4096
     import torch

@@ -446,11 +446,10 @@ hipError_t launch(K kern, int grid, int lds_bytes, const SliceArgs &a, hipStream
 }  // namespace
 
 bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp) {
-  // byte offsets of the buffer loads, including one tile of rows past the
-  // end (those read as zero), must stay below 2^32
-  const int64_t lim = int64_t(1) << 32;
-  return bf16 && d % 64 == 0 && (V + 512) * d * 2 < lim &&
-         (C + 512) * ldp * 2 < lim && (C + 512) * d * 2 < lim;
+  // Within a tile the buffer offsets are (row < 256) * pitch + k bytes, so
+  // pitches (ldp, the slice's token count, d) stay far below 2^31 / 512.
+  const int64_t lim = int64_t(1) << 22;
+  return bf16 && d % 64 == 0 && d < lim && ldp < lim && C < lim && V < (int64_t(1) << 31);
 }
 
 int dh_splits(int C, int d, int nseg, bool fast, int bn) {

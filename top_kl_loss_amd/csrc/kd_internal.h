@@ -77,9 +77,9 @@ constexpr int G1_BM = 128, G1_BN = SEG;   // logits:  C x V, K = d
 constexpr int DH_BM = 128, DH_BN = 128;   // dH:      C x d, K = V (split)
 constexpr int DW_BM = 128, DW_BN = 128;   // dW:      V x d, K = C
 
-// The tuned bf16 kernels (kd_gemm_fast.hip) need d % 64 == 0 and every
-// operand buffer below 4 GiB (32-bit buffer offsets); otherwise the generic
-// kernels (kd_gemm.hip) run.
+// The tuned bf16 kernels (kd_gemm_fast.hip) need d % 64 == 0 (and pitches
+// below 2^22 elements, so that offsets inside a 256-row tile fit the 32-bit
+// buffer offsets); otherwise the generic kernels (kd_gemm.hip) run.
 bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp);
 int dh_splits(int C, int d, int nseg, bool fast, int bn);
 int fast_dh_splits(int C, int d, int nseg, int bn);

@@ -52,10 +52,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_res(const void *base,
                                            (int)n, 0x00020000);
 }
 
+// Buffer resource over the rows mn0.. of a row-major operand (pitch ld
+// elements, `bytes` in the whole buffer): per-tile offsets stay small, so the
+// operand itself may exceed the 4 GiB reach of 32-bit buffer offsets; rows at
+// or past the buffer's end read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_res(const void *base, uint64_t bytes,
+                                                                int64_t ld, int mn0) {
+  const uint64_t skip = (uint64_t)mn0 * (uint64_t)ld * 2;
+  return make_res(reinterpret_cast<const char *>(base) + skip, bytes > skip ? bytes - skip : 0);
+}
+
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ------------------------------------------------------------- operand copy
-// K-contiguous operand, element (mn, k) at byte (mn * ld + k) * 2 of `res`,
+// K-contiguous operand, element (mn, k) at byte (mn * ld + k) * 2 of the
+// buffer (the resource starts at row mn0),
 // ROWS rows copied by NW waves (index w among them), each issuing
 // ROWS/8/NW instructions of 1 KiB (8 rows x 128 B) per k-step.
 template <int NW, int ROWS = 256>
@@ -67,14 +78,14 @@ struct CopyK {
   int w;
   __device__ __forceinline__ void init(const void *base, uint64_t bytes, int64_t ld,
                                        int mn0, int w_, int lane) {
-    res = make_res(base, bytes);
+    res = make_tile_res(base, bytes, ld, mn0);
     w = w_;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       const int p = (w * N + n) * 64 + lane;  // 16-byte position in the tile
       const int row = p >> 3, pc = p & 7;
       const int lc = pc ^ swz(row);
-      off[n] = (uint32_t)(((int64_t)(mn0 + row) * ld + lc * 8) * 2);
+      off[n] = (uint32_t)(((int64_t)row * ld + lc * 8) * 2);
     }
   }
   __device__ __forceinline__ void issue(char *tile, int k0) {
@@ -264,7 +275,8 @@ using Tall = Shape<6, 10>;    // 192 x 320 (N = d multiple of 320)
 static_assert(Tall::LDS <= 160 * 1024, "LDS");
 
 // ROWS rows of a K-contiguous operand, element (mn, k) at byte
-// (mn * ld + k) * 2 of `res`; wave w issues ROWS / 32 instructions of 1 KiB.
+// (mn * ld + k) * 2 of the buffer (the resource starts at row mn0); wave w
+// issues ROWS / 32 instructions of 1 KiB.
 template <int ROWS>
 struct Copy {
   static constexpr int N = ROWS / 32;
@@ -273,13 +285,13 @@ struct Copy {
   int w;
   __device__ __forceinline__ void init(const void *base, uint64_t bytes, int64_t ld, int mn0,
                                        int w_, int lane) {
-    res = make_res(base, bytes);
+    res = make_tile_res(base, bytes, ld, mn0);
     w = w_;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       const int p = (w * N + n) * 64 + lane;
       const int row = p >> 3, pc = p & 7;
-      off[n] = (uint32_t)(((int64_t)(mn0 + row) * ld + (pc ^ swz4(row)) * 8) * 2);
+      off[n] = (uint32_t)(((int64_t)row * ld + (pc ^ swz4(row)) * 8) * 2);
     }
   }
   __device__ __forceinline__ void issue(char *tile, int k0, int n) {
