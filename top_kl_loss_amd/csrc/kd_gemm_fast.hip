@@ -1,7 +1,6 @@
 // bf16 matrix-core GEMMs of the fused, chunked top-K KL loss, tuned for
-// gfx950 (used when d is a multiple of 64 and the operand buffers fit 32-bit
-// byte offsets; other shapes and fp32 inputs take the generic kernels of
-// kd_gemm.hip, which compute the same thing).
+// gfx950 (used when d is a multiple of 64; other shapes and fp32 inputs take
+// the generic kernels of kd_gemm.hip, which compute the same thing).
 //
 //  logits:  Z = H_c W^T      (C x V, K = d)   + softmax-statistics epilogue
 //  dH:      dH_c = G W       (C x d, K = V)   split-K over the vocabulary
