@@ -12,6 +12,7 @@ from .kd_oracle import (  # noqa: F401
     row_lse,
     rows_loss_and_dh,
     scattered_teacher,
+    slice_terms,
     teacher_distribution,
     teacher_entropy,
 )

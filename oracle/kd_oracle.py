@@ -59,6 +59,7 @@ __all__ = [
     "teacher_distribution",
     "log_softmax_rows",
     "kd_topk_kl",
+    "slice_terms",
     "row_lse",
     "rows_loss_and_dh",
     "dw_rows",
@@ -139,11 +140,9 @@ def kd_topk_kl(H, W, topk_idx, topk_logit, mask, tau, chunk=None):
     tau = float(tau)
     m = _mask_vector(mask, T)
     n_valid = float(m.sum())
-    # R3: loss scale tau^2/N and gradient scale tau/N; N = 0 gives zeros.
+    # R3: loss scale tau^2/N (and gradient scale tau/N, in slice_terms);
+    # N = 0 gives zeros.
     loss_scale = tau * tau / n_valid if n_valid > 0 else 0.0
-    grad_scale = tau / n_valid if n_valid > 0 else 0.0
-
-    q, log_q = teacher_distribution(topk_logit, tau)
     chunk = T if chunk is None else max(1, min(int(chunk), T))
 
     row_loss = np.zeros(T)
@@ -152,20 +151,12 @@ def kd_topk_kl(H, W, topk_idx, topk_logit, mask, tau, chunk=None):
     dW = np.zeros((V, d))
     for c0 in range(0, T, chunk):
         c1 = min(T, c0 + chunk)
-        rows = np.arange(c0, c1)
-        z = H[c0:c1] @ W.T                               # dense slice [C, V]
-        log_p, lse = log_softmax_rows(z / tau)           # R2
+        rl, lse, dH[c0:c1], dW_part = slice_terms(
+            H[c0:c1], W, topk_idx[c0:c1], topk_logit[c0:c1],
+            m[c0:c1], tau, n_valid)
+        row_loss[c0:c1] = rl
         lse_all[c0:c1] = lse
-        ids = topk_idx[c0:c1]
-        log_p_at = log_p[np.arange(c1 - c0)[:, None], ids]   # [C, K]
-        # forward KL(q || p) on the teacher's support, one value per row
-        kl = (q[c0:c1] * (log_q[c0:c1] - log_p_at)).sum(axis=1)
-        row_loss[c0:c1] = m[rows] * kl
-        # dL/dz = tau/N * mask * (p - q_scat)
-        G = np.exp(log_p) - scattered_teacher(ids, q[c0:c1], V)
-        G *= (grad_scale * m[rows])[:, None]
-        dH[c0:c1] = G @ W
-        dW += G.T @ H[c0:c1]
+        dW += dW_part
     loss = loss_scale * row_loss.sum()
     return {
         "loss": loss,
@@ -175,6 +166,38 @@ def kd_topk_kl(H, W, topk_idx, topk_logit, mask, tau, chunk=None):
         "lse": lse_all,
         "n_valid": n_valid,
     }
+
+
+def slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
+    """One slice of the chunked loss (the body of ``kd_topk_kl``'s loop).
+
+    For the token rows given, with the whole batch's valid-token count
+    ``n_valid``: the dense logits z = H_rows W^T of the slice, the student
+    log-softmax over the vocabulary, the forward KL against the teacher's
+    top-K distribution, and the logit gradient G = tau/N mask (p - q_scat)
+    with its two products.  Returns (row_loss = mask*KL [R], lse [R] of z/tau,
+    dH rows G W [R, d], the slice's dW contribution G^T H_rows [V, d]), all
+    fp64.  Slices of a batch are independent given n_valid, so a full-size
+    batch can be evaluated slice by slice with the results summed.
+    """
+    H_rows = _f64(H_rows)
+    W = _f64(W)
+    tau = float(tau)
+    R = H_rows.shape[0]
+    V = W.shape[0]
+    m = _mask_vector(mask_rows, R)
+    grad_scale = tau / n_valid if n_valid > 0 else 0.0
+    q, log_q = teacher_distribution(logit_rows, tau)       # R1
+    ids = np.asarray(idx_rows, dtype=np.int64)
+    z = H_rows @ W.T                                       # dense slice [R, V]
+    log_p, lse = log_softmax_rows(z / tau)                 # R2
+    log_p_at = log_p[np.arange(R)[:, None], ids]           # [R, K]
+    # forward KL(q || p) on the teacher's support, one value per row
+    kl = (q * (log_q - log_p_at)).sum(axis=1)
+    # dL/dz = tau/N * mask * (p - q_scat)
+    G = np.exp(log_p) - scattered_teacher(ids, q, V)
+    G *= (grad_scale * m)[:, None]
+    return m * kl, lse, G @ W, G.T @ H_rows
 
 
 def row_lse(H_rows, W, tau, rows_per_block=256):
@@ -200,21 +223,9 @@ def rows_loss_and_dh(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
     count of the mask), so sampled rows of a full-size problem can be
     checked one by one.  Returns (row_loss [R] = mask*KL, dH [R,d]).
     """
-    H_rows = _f64(H_rows)
-    W = _f64(W)
-    tau = float(tau)
-    R = H_rows.shape[0]
-    m = _mask_vector(mask_rows, R)
-    grad_scale = tau / n_valid if n_valid > 0 else 0.0
-    q, log_q = teacher_distribution(logit_rows, tau)
-    z = H_rows @ W.T
-    log_p, _ = log_softmax_rows(z / tau)
-    ids = np.asarray(idx_rows, dtype=np.int64)
-    log_p_at = log_p[np.arange(R)[:, None], ids]
-    kl = (q * (log_q - log_p_at)).sum(axis=1)
-    G = np.exp(log_p) - scattered_teacher(ids, q, W.shape[0])
-    G *= (grad_scale * m)[:, None]
-    return m * kl, G @ W
+    rl, _, dH_rows, _ = slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows,
+                                    tau, n_valid)
+    return rl, dH_rows
 
 
 def dw_rows(H, W, topk_idx, topk_logit, mask, tau, lse, v_rows):
@@ -286,11 +297,13 @@ def entropy_filter_mask(topk_logit, mask, tau, mode, param):
     """Token mask of the entropy filter (asibiont.com article, sections
     "Distillation Token Filtering" and "A Concrete Implementation Sketch"):
 
-    * mode "above": valid and entropy > param (the sketch's
-      ``attention_mask.bool() & (entropy > entropy_threshold)``);
+    * mode "above": a token is kept when it is valid and its teacher entropy
+      exceeds param (the sketch combines the padding mask with a strict
+      entropy threshold);
     * mode "top_fraction": among the N valid tokens, the n = floor(param*N
-      + 1/2) with the highest entropy, equal entropies by lower index
-      ("keep a fixed percentage of tokens with the highest entropy").
+      + 1/2) with the highest entropy, equal entropies by lower index (the
+      section's alternative of retaining a set share of the batch's most
+      uncertain tokens).
     """
     ent = teacher_entropy(topk_logit, tau)
     T = ent.shape[0]

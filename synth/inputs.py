@@ -164,9 +164,10 @@ def exact_mask(case, T, frac):
 
 def make_case(name="custom", *, case, T, d, V, K, dtype, tau=1.0,
               mask_frac=0.0, chunk=None, cache="uniform", logit_scale=1.0,
-              teacher_device=None, h_std=1.0):
-    """Draw one problem.  ``cache`` is "uniform" (random distinct ids) or
-    "teacher" (top-K of a random teacher head)."""
+              teacher_device=None, h_std=1.0, self_noise=0.0):
+    """Draw one problem.  ``cache`` is "uniform" (random distinct ids),
+    "teacher" (top-K of a random teacher head) or "self" (top-K of the
+    student's own logits, plus N(0, self_noise^2) on each logit)."""
     H = _normal(case, 0, (T, d), h_std)
     W = _normal(case, 1, (V, d), 1.0 / np.sqrt(d))
     H_bits = W_bits = None
@@ -183,6 +184,16 @@ def make_case(name="custom", *, case, T, d, V, K, dtype, tau=1.0,
         Wt = _normal(case, 2, (V, d), 1.0 / np.sqrt(d))
         idx, logit = teacher_topk(H, Wt, K, device=teacher_device)
         del Wt
+    elif cache == "self":
+        # the student's own top-K logits plus N(0, self_noise^2): a teacher
+        # the student already matches up to the noise and the mass outside
+        # its top K (the near-converged regime, KL close to 0)
+        idx, logit = teacher_topk(H, W, K, device=teacher_device)
+        if self_noise:
+            logit = logit + _normal(case, 5, logit.shape, self_noise)
+            order = np.argsort(-logit, axis=1, kind="stable")
+            idx = np.take_along_axis(idx, order, 1)
+            logit = np.take_along_axis(logit, order, 1)
     else:
         raise ValueError(cache)
     if logit_scale != 1.0:

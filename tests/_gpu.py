@@ -114,3 +114,70 @@ def check_topk(x, ids, vals, K, exact=False, rows=None):
             zk1 = np.sort(z[t])[::-1][K]
             sure = o_ids[t][o_vals[t] > zk1 + 2 * tol]
             assert set(sure.tolist()) <= set(row.tolist()), f"{where}: missing ids"
+
+
+# ---------------------------------------------- near-converged loss tolerance
+U32 = 2.0 ** -24     # fp32 unit roundoff
+
+
+def kl_rounding_floor_rows(x):
+    """Per-row absolute KL error that fp32 arithmetic alone can cause, for
+    the loss bars near KL = 0 (where a relative bar cannot hold).  Twice the
+    sum of two first-order terms, plus 8 u:
+      * the logits: an fp32 dot product over d terms is off by about
+        sqrt(d) * u * max|z|, and KL_t moves by sum_v (p - q_scat) dz / tau
+        to first order;
+      * the log-probabilities: KL_t = sum_k q_k (log q_k - log p_k) is
+        formed from values rounded to u * |log q_k| and u * |log p_k|;
+      * the normaliser: log of a sum of exponentials (>= 1 after the shift
+        by the maximum), each rounded relative to its size, is off by a few u
+        in absolute terms however small KL_t is.
+    Computed densely in fp64 from the inputs, for oracle-sized cases."""
+    H = np.asarray(x.H, np.float64)
+    W = np.asarray(x.W, np.float64)
+    z = H @ W.T / x.tau
+    zmax = np.abs(z).max(axis=1)
+    z -= z.max(axis=1, keepdims=True)
+    logp = z - np.log(np.exp(z).sum(axis=1, keepdims=True))
+    p = np.exp(logp)
+    u = np.asarray(x.topk_logit, np.float64) / x.tau
+    u -= u.max(axis=1, keepdims=True)
+    logq = u - np.log(np.exp(u).sum(axis=1, keepdims=True))
+    q = np.exp(logq)
+    qs = np.zeros_like(p)
+    np.add.at(qs, (np.repeat(np.arange(x.T), x.K), x.topk_idx.reshape(-1)), q.reshape(-1))
+    logp_at = np.take_along_axis(logp, x.topk_idx.astype(np.int64), 1)
+    logits = np.abs(p - qs).sum(axis=1) * np.sqrt(x.d) * U32 * zmax
+    logs = U32 * (q * (np.abs(logq) + np.abs(logp_at))).sum(axis=1)
+    m = np.ones(x.T) if x.mask is None else (x.mask != 0).astype(np.float64)
+    return m * (2.0 * (logits + logs) + 8.0 * U32)
+
+
+def loss_rounding_floor(x, floor_rows):
+    """The loss's share of the per-row floors: tau^2 / N * sum_t floor_t."""
+    n = x.n_valid
+    return x.tau ** 2 * float(floor_rows.sum()) / n if n > 0 else 0.0
+
+
+def fp32_logit_grad_floor(x, ref):
+    """(dH, dW) max relative errors that fp32 logits alone cause near KL = 0:
+    the gradients evaluated in fp64 from z = H W^T rounded by a float32
+    matrix product (numpy), against the oracle's.  Near the minimum the
+    logit gradient is a small difference p - q_scat, and an fp32 logit error
+    dz moves p by p dz / tau, so a relative bar meets this floor; the fp32
+    near-converged tests add twice it to the 1e-4 bar."""
+    z = (np.asarray(x.H, np.float32) @ np.asarray(x.W, np.float32).T).astype(np.float64)
+    s = z / x.tau
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    u = np.asarray(x.topk_logit, np.float64) / x.tau
+    q = np.exp(u - u.max(axis=1, keepdims=True))
+    q /= q.sum(axis=1, keepdims=True)
+    g = p
+    np.subtract.at(g, (np.repeat(np.arange(x.T), x.K), x.topk_idx.reshape(-1)), q.reshape(-1))
+    m = np.ones(x.T) if x.mask is None else (x.mask != 0).astype(np.float64)
+    g *= (x.tau / max(m.sum(), 1.0) * m)[:, None]
+    dH = g @ np.asarray(x.W, np.float64)
+    dW = g.T @ np.asarray(x.H, np.float64)
+    return maxrel(dH, ref["dH"]), maxrel(dW, ref["dW"])

@@ -132,3 +132,36 @@ def test_autograd_through_a_student_head_and_a_training_step():
         opt.step()
         losses.append(float(loss.item()))
     assert all(b < a for a, b in zip(losses, losses[1:])), losses
+
+
+def test_training_step_on_one_stream_without_host_synchronisation():
+    # torch ops -> loss -> backward -> torch ops, all queued on one side
+    # stream: the library calls return while the stream is still busy (no
+    # host synchronisation inside), and the results match the oracle
+    import torch
+    from top_kl_loss_amd.autograd import topk_kl_loss
+    x = synth.make_case("ag_stream", case=63, T=384, d=192, V=3000, K=20,
+                        dtype="bf16", tau=1.5, mask_frac=0.1, chunk=128)
+    dev = G.to_device(x)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    busy = []
+    with torch.cuda.stream(s):
+        # exact in bf16 (powers of two): the inputs come out of torch kernels
+        H = ((dev["H"] * 4.0) * 0.25).requires_grad_(True)
+        W = (dev["W"] * 1.0).requires_grad_(True)
+        torch.cuda._sleep(100_000_000)     # keeps the stream busy for a while
+        loss = topk_kl_loss(H, W, dev["topk_idx"], dev["topk_logit"],
+                            dev["mask"], x.tau, x.chunk)
+        busy.append(not s.query())
+        (loss * 3.0).backward()
+        busy.append(not s.query())
+        gH = H.grad.float() * 1.0
+        gW = W.grad.float() * 1.0
+        lv = loss * 1.0
+    s.synchronize()
+    assert all(busy), busy
+    ref = orc.kd_topk_kl(x.H, x.W, x.topk_idx, x.topk_logit, x.mask, x.tau)
+    G.assert_loss_close(float(lv.item()), ref["loss"], x.dtype)
+    G.assert_grad_close(G.to_np(gH), 3.0 * ref["dH"], x.dtype, "H.grad")
+    G.assert_grad_close(G.to_np(gW), 3.0 * ref["dW"], x.dtype, "W.grad")

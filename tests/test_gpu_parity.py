@@ -176,12 +176,11 @@ def test_bf16_tuned_path_largest_k():
 
 
 def test_concurrent_calls_on_two_streams():
-    # two calls in flight at once on two streams of the library's runtime,
-    # each with its own workspace and outputs, give the results of the same
-    # calls made one after the other (bitwise)
+    # two calls in flight at once on two torch streams, each with its own
+    # workspace and outputs, give the results of the same calls made one
+    # after the other (bitwise)
     import torch
     import top_kl_loss_amd as kd
-    from top_kl_loss_amd import hip
     xa = synth.make_case("conc_a", case=35, T=520, d=192, V=4000, K=40,
                          dtype="bf16", tau=1.0, mask_frac=0.05, chunk=256)
     xb = synth.make_case("conc_b", case=36, T=300, d=256, V=3000, K=60,
@@ -189,16 +188,19 @@ def test_concurrent_calls_on_two_streams():
     da, db = G.to_device(xa), G.to_device(xb)
     ref_a = G.run(da, xa.tau, xa.chunk)
     ref_b = G.run(db, xb.tau, xb.chunk)
-    sa, sb = hip.Stream(), hip.Stream()
-    out_a = kd.kd_topk_kl_fwd_bwd(da["H"], da["W"], da["topk_idx"], da["topk_logit"],
-                                  da["mask"], xa.tau, xa.chunk, stream=sa.value,
-                                  sync=False)
-    out_b = kd.kd_topk_kl_fwd_bwd(db["H"], db["W"], db["topk_idx"], db["topk_logit"],
-                                  db["mask"], xb.tau, xb.chunk, stream=sb.value,
-                                  sync=False)
-    sa.synchronize()
-    sb.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    outs = []
+    for s, d, x in ((sa, da, xa), (sb, db, xb)):
+        s.wait_stream(main)  # the inputs were written on the main stream
+        ws = torch.empty(kd.kd_topk_kl_workspace_size(x.T, x.d, x.V, x.K, x.chunk,
+                                                      kd.KD_BF16),
+                         dtype=torch.uint8, device="cuda")
+        ws.record_stream(s)
+        outs.append(kd.kd_topk_kl_fwd_bwd(d["H"], d["W"], d["topk_idx"],
+                                          d["topk_logit"], d["mask"], x.tau,
+                                          x.chunk, workspace=ws, stream=s))
     torch.cuda.synchronize()
-    for got, want in ((out_a, ref_a), (out_b, ref_b)):
+    for got, want in ((outs[0], ref_a), (outs[1], ref_b)):
         for u, v in zip(got, want):
             assert torch.equal(u, v)

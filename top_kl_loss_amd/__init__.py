@@ -1,14 +1,16 @@
 """Python binding of libkdtopk.so, the MI355X fused chunked top-K KL loss.
 
 Argument marshalling only: every step of the loss runs in the HIP kernels of
-the C library (``include/kd_topk_kl.h``).  PyTorch provides device memory.
-There is no fallback: if the library is missing or cannot be loaded, every
-call raises.
+the C library (``include/kd_topk_kl.h``).  PyTorch provides device memory and
+streams.  There is no fallback: if the library is missing or cannot be
+loaded, every call raises.
 
-PyTorch-ROCm carries its own HIP runtime, separate from the one the library
-is linked against, so the binding orders the two by host synchronisation:
-torch's pending work is finished before the library call, and the library's
-stream is synchronised before results are handed back (``sync=True``).
+The library is loaded after torch, so its dependency on the HIP runtime
+resolves (by soname) to the runtime torch has already loaded: one runtime
+per process, whose streams and events both sides share.  Every call is
+enqueued on a torch stream (by default the current one) without any host
+synchronisation, and every temporary buffer is allocated on that stream, so
+torch's caching allocator reuses it only after the call's kernels.
 """
 from __future__ import annotations
 
@@ -64,7 +66,11 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(
             f"{path} is not built; run `python -m top_kl_loss_amd.build` "
             "(needs ROCm hipcc)")
+    # torch first: its HIP runtime (soname libamdhip64.so.7) is then the one
+    # the library's dependency binds to, so torch's streams are valid here.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
+    _check_single_runtime()
     c = ctypes
     lib.kd_topk_kl_workspace_size.argtypes = [
         c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_int,
@@ -115,6 +121,23 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
+def _check_single_runtime():
+    """Raise if two HIP runtimes are mapped into the process (e.g. the library
+    was loaded through ctypes before torch): stream and event handles of one
+    are meaningless to the other."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f
+                     if "libamdhip64" in line.rsplit("/", 1)[-1]}
+    except OSError:  # pragma: no cover - not Linux
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise RuntimeError(
+            "two HIP runtimes are loaded (" + ", ".join(sorted(real)) + "); "
+            "import torch before loading libkdtopk.so")
+
+
 def kd_status_string(status: int) -> str:
     return load_library().kd_status_string(int(status)).decode()
 
@@ -152,9 +175,49 @@ def _dtype_code(t):
     raise TypeError(f"H/W must be bfloat16 or float32, got {t.dtype}")
 
 
+def _torch_stream(dev, stream):
+    """The torch stream a call runs on: the current stream of ``dev`` (None),
+    a ``torch.cuda.Stream``, or a raw hipStream_t handle (int) of the same
+    runtime, wrapped as an external stream."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
+class _Call:
+    """Context of one library call: device and stream guards, so that every
+    tensor allocated inside is owned by the call's stream; on exit the
+    stream is synchronised only when ``sync`` is set."""
+
+    def __init__(self, dev, stream, sync):
+        import torch
+        self.dev = dev
+        self.ts = _torch_stream(dev, stream)
+        self.sync = sync
+        self._guards = (torch.cuda.device(dev), torch.cuda.stream(self.ts))
+
+    @property
+    def handle(self):
+        return self.ts.cuda_stream
+
+    def __enter__(self):
+        for g in self._guards:
+            g.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        for g in reversed(self._guards):
+            g.__exit__(*exc)
+        if exc[0] is None and self.sync:
+            self.ts.synchronize()
+        return False
+
+
 def _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk):
-    """Validates the loss inputs; returns (T, d, V, K, chunk, dtype code,
-    mask as uint8 or None)."""
+    """Validates the loss inputs; returns (T, d, V, K, chunk, dtype code)."""
     import torch
     T, d = H.shape
     V = W.shape[0]
@@ -169,16 +232,22 @@ def _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk):
         raise ValueError("topk_logit must be float32 [T, K]")
     tensors = [H, W, topk_idx, topk_logit]
     if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.to(torch.uint8)
-        if mask.dtype != torch.uint8 or mask.numel() != T:
+        if mask.dtype not in (torch.bool, torch.uint8) or mask.numel() != T:
             raise ValueError("mask must be uint8/bool [T]")
         tensors.append(mask)
     dev = H.device
     for t in tensors:
         if not t.is_cuda or t.device != dev or not t.is_contiguous():
             raise ValueError("all inputs must be contiguous tensors on one GPU")
-    return T, d, V, K, chunk, dt, mask
+    return T, d, V, K, chunk, dt
+
+
+def _mask_u8(mask):
+    """The mask as uint8 (a bool mask is converted on the call's stream)."""
+    import torch
+    if mask is None or mask.dtype == torch.uint8:
+        return mask
+    return mask.to(torch.uint8)
 
 
 def _workspace(T, d, V, K, chunk, dt, workspace, dev):
@@ -191,120 +260,115 @@ def _workspace(T, d, V, K, chunk, dt, workspace, dev):
     return workspace
 
 
-def _enter(dev):
-    """Orders the library's work after torch's pending work."""
-    import torch
-    from . import hip
-    torch.cuda.synchronize(dev)          # inputs written by torch are ready
-    hip.set_device(dev.index if dev.index is not None else 0)
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
 
 
-def _leave(stream, sync):
-    if sync:
-        from . import hip
-        hip.synchronize(stream)
+_STREAM_DOC = """
+    ``stream`` is None (torch's current stream on the inputs' device), a
+    ``torch.cuda.Stream`` or a raw hipStream_t handle.  The work is enqueued
+    there with no host synchronisation, and outputs and temporaries are
+    allocated on that stream, so torch work queued on it afterwards sees the
+    results; ``sync=True`` also waits for the stream before returning."""
 
 
 def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
                        chunk=None, flags=0, *, dW=None, row_loss=True,
-                       workspace=None, stream=None, sync=True):
+                       workspace=None, stream=None, sync=False):
     """Loss, per-row KL, dH and dW of the top-K KL loss on the GPU.
 
     H [T,d] and W [V,d] (bf16 or fp32), topk_idx [T,K] int32, topk_logit
     [T,K] fp32 and mask [T] (uint8/bool or None) are CUDA tensors.  Outputs
     are allocated here (``dW`` may be passed in, e.g. with
     KD_FLAG_ACCUMULATE_DW).  Returns (loss[1], row_loss[T] or None, dH, dW).
-
-    ``stream`` is a stream handle of the library's HIP runtime
-    (``top_kl_loss_amd.hip.Stream().value``) or None for its null stream.
-    With ``sync=False`` the call returns as soon as the work is enqueued;
-    the caller must then keep every tensor alive and synchronise the stream
-    (``top_kl_loss_amd.hip.synchronize``) before torch touches the results.
     """
     import torch
     lib = load_library()
-    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    T, d, V, K, chunk, dt = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
     dev = H.device
-    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    loss = torch.empty(1, **f32)
-    rl = torch.empty(T, **f32) if row_loss else None
-    dH = torch.empty(T, d, **f32)
-    if dW is None:
-        dW = torch.empty(V, d, **f32)
-    elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
-        raise ValueError("dW must be float32 [V, d]")
-    _enter(dev)
-    _check(lib.kd_topk_kl_fwd_bwd(
-        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
-        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
-        T, d, V, K, float(tau), chunk, int(flags), loss.data_ptr(),
-        rl.data_ptr() if rl is not None else None, dH.data_ptr(),
-        dW.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
-    _leave(stream, sync)
+    if dW is not None and (dW.shape != (V, d) or dW.dtype != torch.float32
+                           or not dW.is_contiguous() or dW.device != dev):
+        raise ValueError("dW must be float32 [V, d] on H's device")
+    with _Call(dev, stream, sync) as call:
+        mask = _mask_u8(mask)
+        workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        loss = torch.empty(1, **f32)
+        rl = torch.empty(T, **f32) if row_loss else None
+        dH = torch.empty(T, d, **f32)
+        if dW is None:
+            dW = torch.empty(V, d, **f32)
+        _check(lib.kd_topk_kl_fwd_bwd(
+            H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+            topk_logit.data_ptr(), _ptr(mask), T, d, V, K, float(tau), chunk,
+            int(flags), loss.data_ptr(), _ptr(rl), dH.data_ptr(),
+            dW.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            call.handle))
     return loss, rl, dH, dW
+
+
+kd_topk_kl_fwd_bwd.__doc__ += _STREAM_DOC
 
 
 def kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
                    chunk=None, *, row_loss=True, lse=True, workspace=None,
-                   stream=None, sync=True):
+                   stream=None, sync=False):
     """The loss alone.  Returns (loss[1], row_loss[T] or None, lse[T] or
     None); arguments as for kd_topk_kl_fwd_bwd."""
     import torch
     lib = load_library()
-    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    T, d, V, K, chunk, dt = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
     dev = H.device
-    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    loss = torch.empty(1, **f32)
-    rl = torch.empty(T, **f32) if row_loss else None
-    ls = torch.empty(T, **f32) if lse else None
-    _enter(dev)
-    _check(lib.kd_topk_kl_fwd(
-        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
-        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
-        T, d, V, K, float(tau), chunk, loss.data_ptr(),
-        rl.data_ptr() if rl is not None else None,
-        ls.data_ptr() if ls is not None else None,
-        workspace.data_ptr(), workspace.numel(), stream))
-    _leave(stream, sync)
+    with _Call(dev, stream, sync) as call:
+        mask = _mask_u8(mask)
+        workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        loss = torch.empty(1, **f32)
+        rl = torch.empty(T, **f32) if row_loss else None
+        ls = torch.empty(T, **f32) if lse else None
+        _check(lib.kd_topk_kl_fwd(
+            H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+            topk_logit.data_ptr(), _ptr(mask), T, d, V, K, float(tau), chunk,
+            loss.data_ptr(), _ptr(rl), _ptr(ls), workspace.data_ptr(),
+            workspace.numel(), call.handle))
     return loss, rl, ls
 
 
 def kd_topk_kl_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
                    chunk=None, flags=0, grad_loss=None, *, dW=None,
-                   workspace=None, stream=None, sync=True):
+                   workspace=None, stream=None, sync=False):
     """dH and dW (fp32) of grad_loss * loss.  ``grad_loss`` is None (1) or a
-    one-element fp32 CUDA tensor.  Returns (dH, dW)."""
+    one-element fp32 CUDA tensor.  Returns (dH, dW); other arguments as for
+    kd_topk_kl_fwd_bwd."""
     import torch
     lib = load_library()
-    T, d, V, K, chunk, dt, mask = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    T, d, V, K, chunk, dt = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
     dev = H.device
-    if grad_loss is not None:
-        if (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1
-                or grad_loss.device != dev):
-            raise ValueError("grad_loss must be one float32 value on H's device")
-        grad_loss = grad_loss.contiguous()
-    workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dH = torch.empty(T, d, **f32)
-    if dW is None:
-        dW = torch.empty(V, d, **f32)
-    elif dW.shape != (V, d) or dW.dtype != torch.float32 or not dW.is_contiguous():
-        raise ValueError("dW must be float32 [V, d]")
-    _enter(dev)
-    _check(lib.kd_topk_kl_bwd(
-        H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
-        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
-        T, d, V, K, float(tau), chunk, int(flags),
-        grad_loss.data_ptr() if grad_loss is not None else None,
-        dH.data_ptr(), dW.data_ptr(), workspace.data_ptr(), workspace.numel(),
-        stream))
-    _leave(stream, sync)
+    if grad_loss is not None and (grad_loss.dtype != torch.float32
+                                  or grad_loss.numel() != 1
+                                  or grad_loss.device != dev):
+        raise ValueError("grad_loss must be one float32 value on H's device")
+    if dW is not None and (dW.shape != (V, d) or dW.dtype != torch.float32
+                           or not dW.is_contiguous() or dW.device != dev):
+        raise ValueError("dW must be float32 [V, d] on H's device")
+    with _Call(dev, stream, sync) as call:
+        mask = _mask_u8(mask)
+        if grad_loss is not None:
+            grad_loss = grad_loss.contiguous()
+        workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        dH = torch.empty(T, d, **f32)
+        if dW is None:
+            dW = torch.empty(V, d, **f32)
+        _check(lib.kd_topk_kl_bwd(
+            H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+            topk_logit.data_ptr(), _ptr(mask), T, d, V, K, float(tau), chunk,
+            int(flags), _ptr(grad_loss), dH.data_ptr(), dW.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), call.handle))
     return dH, dW
 
 
-def kd_grad_cast(src, dtype, scale=None, *, out=None, stream=None, sync=True):
+def kd_grad_cast(src, dtype, scale=None, *, out=None, stream=None, sync=False):
     """src (fp32 CUDA tensor) times scale (None or a one-element fp32 CUDA
     tensor) as a new tensor of torch dtype ``dtype`` (bfloat16 or float32),
     or into ``out``."""
@@ -315,17 +379,16 @@ def kd_grad_cast(src, dtype, scale=None, *, out=None, stream=None, sync=True):
     code = KD_BF16 if dtype == torch.bfloat16 else KD_F32 if dtype == torch.float32 else None
     if code is None:
         raise TypeError(f"unsupported dtype {dtype}")
-    if out is None:
-        out = torch.empty(src.shape, dtype=dtype, device=src.device)
-    elif out.dtype != dtype or out.shape != src.shape or not out.is_contiguous():
+    if out is not None and (out.dtype != dtype or out.shape != src.shape
+                            or not out.is_contiguous()):
         raise ValueError("out must match src's shape and the dtype")
     if scale is not None and (scale.dtype != torch.float32 or scale.numel() != 1):
         raise ValueError("scale must be one float32 value")
-    _enter(src.device)
-    _check(lib.kd_grad_cast(src.data_ptr(), out.data_ptr(), code, src.numel(),
-                            scale.data_ptr() if scale is not None else None,
-                            stream))
-    _leave(stream, sync)
+    with _Call(src.device, stream, sync) as call:
+        if out is None:
+            out = torch.empty(src.shape, dtype=dtype, device=src.device)
+        _check(lib.kd_grad_cast(src.data_ptr(), out.data_ptr(), code, src.numel(),
+                                _ptr(scale), call.handle))
     return out
 
 
@@ -339,7 +402,7 @@ def kd_teacher_topk_workspace_size(T, d, V, K, chunk, dtype) -> int:
 
 
 def kd_teacher_topk(H, W, K, chunk=None, *, workspace=None, stream=None,
-                    sync=True):
+                    sync=False):
     """Teacher top-K cache on the GPU: for each row of z = H W^T, the K
     largest logits (fp32) and their ids (int32), by logit descending and
     equal logits by id ascending.  H [T,d] and W [V,d] are bf16 or fp32
@@ -358,21 +421,17 @@ def kd_teacher_topk(H, W, K, chunk=None, *, workspace=None, stream=None,
         if not t.is_cuda or t.device != dev or not t.is_contiguous():
             raise ValueError("H and W must be contiguous tensors on one GPU")
     ws_bytes = kd_teacher_topk_workspace_size(T, d, V, K, chunk, dt)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    elif workspace.numel() < ws_bytes:
-        raise ValueError("workspace too small")
-    ids = torch.empty(T, int(K), dtype=torch.int32, device=dev)
-    vals = torch.empty(T, int(K), dtype=torch.float32, device=dev)
-    from . import hip
-    torch.cuda.synchronize(dev)
-    hip.set_device(dev.index if dev.index is not None else 0)
-    _check(lib.kd_teacher_topk(
-        H.data_ptr(), W.data_ptr(), dt, T, d, V, int(K), chunk,
-        ids.data_ptr(), vals.data_ptr(), workspace.data_ptr(),
-        workspace.numel(), stream))
-    if sync:
-        hip.synchronize(stream)
+    with _Call(dev, stream, sync) as call:
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        elif workspace.numel() < ws_bytes:
+            raise ValueError("workspace too small")
+        ids = torch.empty(T, int(K), dtype=torch.int32, device=dev)
+        vals = torch.empty(T, int(K), dtype=torch.float32, device=dev)
+        _check(lib.kd_teacher_topk(
+            H.data_ptr(), W.data_ptr(), dt, T, d, V, int(K), chunk,
+            ids.data_ptr(), vals.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), call.handle))
     return ids, vals
 
 
@@ -383,7 +442,7 @@ def kd_entropy_filter_workspace_size(T) -> int:
 
 
 def kd_entropy_filter(topk_logit, mask=None, tau=1.0, mode="above", param=0.5,
-                      *, entropy=True, workspace=None, stream=None, sync=True):
+                      *, entropy=True, workspace=None, stream=None, sync=False):
     """Token mask from the teacher's entropy over its K cached logits (see
     the C header).  mode "above": keep valid tokens with entropy > param;
     "top_fraction": keep round(param * N) valid tokens of highest entropy.
@@ -399,24 +458,21 @@ def kd_entropy_filter(topk_logit, mask=None, tau=1.0, mode="above", param=0.5,
             not topk_logit.is_contiguous():
         raise ValueError("topk_logit must be a contiguous float32 CUDA tensor")
     dev = topk_logit.device
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.to(torch.uint8)
-        if mask.dtype != torch.uint8 or mask.numel() != T or mask.device != dev:
-            raise ValueError("mask must be uint8/bool [T] on the logits' device")
-        mask = mask.contiguous()
+    if mask is not None and (mask.dtype not in (torch.bool, torch.uint8)
+                             or mask.numel() != T or mask.device != dev):
+        raise ValueError("mask must be uint8/bool [T] on the logits' device")
     ws_bytes = kd_entropy_filter_workspace_size(T)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    elif workspace.numel() < ws_bytes:
-        raise ValueError("workspace too small")
-    out = torch.empty(T, dtype=torch.uint8, device=dev)
-    ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
-    _enter(dev)
-    _check(lib.kd_entropy_filter(
-        topk_logit.data_ptr(), mask.data_ptr() if mask is not None else None,
-        T, K, float(tau), codes[mode], float(param), out.data_ptr(),
-        ent.data_ptr() if ent is not None else None, workspace.data_ptr(),
-        workspace.numel(), stream))
-    _leave(stream, sync)
+    with _Call(dev, stream, sync) as call:
+        if mask is not None:
+            mask = _mask_u8(mask).contiguous()
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        elif workspace.numel() < ws_bytes:
+            raise ValueError("workspace too small")
+        out = torch.empty(T, dtype=torch.uint8, device=dev)
+        ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
+        _check(lib.kd_entropy_filter(
+            topk_logit.data_ptr(), _ptr(mask), T, K, float(tau), codes[mode],
+            float(param), out.data_ptr(), _ptr(ent), workspace.data_ptr(),
+            workspace.numel(), call.handle))
     return out, ent

@@ -49,7 +49,7 @@ struct Layout {
   int C, nseg, ldp, splits;
   bool fast;
   size_t esize;
-  size_t o_scal, o_rowloss, o_q, o_cterm, o_zg, o_sid, o_sslot, o_first,
+  size_t o_scal, o_rowloss, o_q, o_lq, o_zg, o_sid, o_sslot, o_first,
       o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt;
   bool wt;
   int dh_bn, dw_bn;
@@ -92,7 +92,7 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_scal = take(sizeof(kd::Scalars));
   L.o_rowloss = take(sizeof(float) * (size_t)T);
   L.o_q = take(sizeof(float) * C * K);
-  L.o_cterm = take(sizeof(float) * C);
+  L.o_lq = take(sizeof(float) * C * K);
   L.o_zg = take(sizeof(float) * C * K);
   L.o_sid = take(sizeof(int32_t) * C * K);
   L.o_sslot = take(sizeof(int32_t) * C * K);
@@ -222,8 +222,9 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
   a.nseg = L.nseg;
   a.ldp = L.ldp;
   a.inv_tau = 1.0f / tau;
+  a.s2 = a.inv_tau * 1.4426950408889634f;
   a.q = reinterpret_cast<float *>(ws + L.o_q);
-  a.cterm = reinterpret_cast<float *>(ws + L.o_cterm);
+  a.lq = reinterpret_cast<float *>(ws + L.o_lq);
   a.zg = reinterpret_cast<float *>(ws + L.o_zg);
   a.sid = reinterpret_cast<int32_t *>(ws + L.o_sid);
   a.sslot = reinterpret_cast<int32_t *>(ws + L.o_sslot);

@@ -295,24 +295,28 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_logits(SliceArgs a) {
     const int sr = tid / TPR, part = tid % TPR;
     const int r = m0 + (sr / 32) * TL::WTM + tm * 32 + (sr % 32);
     const int c0 = part * CPT;
+    // base-2 units: shift = max(z) s2, P = 2^(z s2 - shift) with one
+    // rounding of the exponent (fma), so P keeps its relative accuracy
+    // however large z s2 itself is
     float v[CPT];
-    float mx = -INFINITY;
+    float zmax = -INFINITY;
 #pragma unroll
     for (int c = 0; c < CPT; c += 4) {
       const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + c0 + c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool ok = n0 + c0 + c + u < a.V;
-        v[c + u] = ok ? z[u] * a.inv_tau : -INFINITY;
-        mx = fmaxf(mx, v[c + u]);
+        v[c + u] = ok ? z[u] : -INFINITY;
+        zmax = fmaxf(zmax, v[c + u]);
       }
     }
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    for (int o = 1; o < TPR; o <<= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o, 64));
+    const float mx = zmax * a.s2;
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const float p = v[c] == -INFINITY ? 0.f : exp2f((v[c] - mx) * LOG2E);
+      const float p = v[c] == -INFINITY ? 0.f : exp2f(fmaf(v[c], a.s2, -mx));
       v[c] = p;
       sum += p;
     }

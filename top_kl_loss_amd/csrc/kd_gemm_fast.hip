@@ -24,9 +24,9 @@ using namespace tile;
 
 // ------------------------------------------------------------ logits GEMM
 // A = H_c, B = W (both K-contiguous), 4-wave tiles.  Epilogue per row and
-// segment: max of z/tau, P = exp(z/tau - max) in bf16, the sum of P, and z
-// itself at the row's teacher ids inside the segment (the student-logit
-// gather).
+// segment, in base-2 units (s2 = log2(e) / tau): the shift max(z) s2,
+// P = 2^(z s2 - shift) in bf16, the sum of P, and z itself at the row's
+// teacher ids inside the segment (the student-logit gather).
 __global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fast_logits(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -87,7 +87,7 @@ void k_fast_logits(SliceArgs a) {
   float *stage = reinterpret_cast<float *>(lds);
   uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
   const int part = tid % TPR;
-  const float s2 = a.inv_tau * LOG2E;
+  const float s2 = a.s2;
   const bool tail = n0 + BN > a.V;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -103,8 +103,10 @@ void k_fast_logits(SliceArgs a) {
     // Thread `part` of a row owns the 8-column groups part, part + 8, ...,
     // so the row's TPR threads store whole 128-byte lines of P together
     // (contiguous 64-byte runs per thread would split every line).
-    // Base-2 units: v = z / tau * log2(e), P = 2^(v - max v); only the
-    // vocabulary's last segment has columns past V (excluded).
+    // Base-2 units: shift = max(z) s2 (s2 = log2(e) / tau) and
+    // P = 2^(z s2 - shift) with the exponent rounded once (fma), so P keeps
+    // its relative accuracy however large z s2 is; only the vocabulary's
+    // last segment has columns past V (excluded).
     float v[RPT][CPT];
     float mx[RPT], sum[RPT];
 #pragma unroll
@@ -120,7 +122,7 @@ void k_fast_logits(SliceArgs a) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int c = j * 8 + 4 * h + u;
-            v[q][c] = z[u] * s2;
+            v[q][c] = z[u];
             if (tail && n0 + col + 4 * h + u >= a.V) v[q][c] = -INFINITY;
             m4[u] = fmaxf(m4[u], v[q][c]);
           }
@@ -134,16 +136,16 @@ void k_fast_logits(SliceArgs a) {
       for (int q = 0; q < RPT; ++q) mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
 #pragma unroll
     for (int q = 0; q < RPT; ++q) {
+      mx[q] *= s2;  // the segment's shift, base-2 units
       float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        // exp2(-inf) = 0 covers the excluded columns
-        const float pv = __builtin_amdgcn_exp2f(v[q][c] - mx[q]);
+        // 2^(-inf) = 0 covers the excluded columns
+        const float pv = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -mx[q]));
         v[q][c] = pv;
         s4[c & 3] += pv;
       }
       sum[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      mx[q] *= LN2;  // the segment maximum of z / tau
     }
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1)

@@ -42,15 +42,16 @@ struct SliceArgs {
   int nseg;    // ceil(V / SEG)
   int ldp;     // nseg * SEG, row pitch of P in elements
   float inv_tau;
+  float s2;          // log2(e) / tau: logits in base-2 units (z s2)
   // workspace views (slice-local, row r)
   float *q;          // [Cmax, K] teacher probabilities
-  float *cterm;      // [Cmax] sum_k q log q
+  float *lq;         // [Cmax, K] log q, from shifted logits (accurate near 0)
   float *zg;         // [Cmax, K] student logit at each teacher slot
   int32_t *sid;      // [Cmax, K] teacher ids sorted ascending
   int32_t *sslot;    // [Cmax, K] slot of each sorted id
   int16_t *first;    // [Cmax, nseg] first sorted position in segment or -1
-  float *mseg;       // [Cmax, nseg] segment max of z/tau (shift)
-  float *sseg;       // [Cmax, nseg] segment sum of exp(z/tau - shift)
+  float *mseg;       // [Cmax, nseg] segment max of z s2 (shift, base-2 units)
+  float *sseg;       // [Cmax, nseg] segment sum of 2^(z s2 - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
   uint16_t *Ht;      // [d, ldh] bf16 H_c^T (tuned path only)
   uint16_t *Gt;      // [ldp, ldh] bf16 G^T (tuned path only)

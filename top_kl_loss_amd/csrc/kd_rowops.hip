@@ -49,11 +49,12 @@ __global__ __launch_bounds__(256) void k_valid_count(const uint8_t *mask, int T,
 }
 
 // Per slice row: teacher distribution q = softmax(topk_logit / tau) over the
-// K cached slots and c = sum_k q log q; the row's ids sorted ascending (with
-// their slots) and, for every vocabulary segment, the first sorted position
-// whose id falls in it (-1 if none).  Also clears the gathered-logit row.
-// Ids outside [0, V) are replaced by INT_MAX so that no later kernel
-// dereferences them.
+// K cached slots and log q, each from the logits shifted by their maximum
+// (one rounding of logit/tau - max, so log q is accurate to its own size);
+// the row's ids sorted ascending (with their slots) and, for every
+// vocabulary segment, the first sorted position whose id falls in it (-1 if
+// none).  Also clears the gathered-logit row.  Ids outside [0, V) are
+// replaced by INT_MAX so that no later kernel dereferences them.
 __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
   __shared__ int32_t s_ids[ROWS_PER_WG][KMAX];
   __shared__ int32_t s_sorted[ROWS_PER_WG][KMAX];
@@ -68,21 +69,17 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
     for (int k = lane; k < K; k += 64) mx = fmaxf(mx, lg[k] * a.inv_tau);
     mx = wave_max(mx);
     float sum = 0.f;
-    for (int k = lane; k < K; k += 64) sum += exp2f((lg[k] * a.inv_tau - mx) * LOG2E);
+    for (int k = lane; k < K; k += 64) sum += expf(fmaf(lg[k], a.inv_tau, -mx));
     sum = wave_sum(sum);
     const float lsum = logf(sum);
-    float cacc = 0.f;
     for (int k = lane; k < K; k += 64) {
-      const float lq = (lg[k] * a.inv_tau - mx) - lsum;
-      const float qk = exp2f(lq * LOG2E);
-      a.q[(size_t)r * K + k] = qk;
-      cacc += qk * lq;
+      const float lq = fmaf(lg[k], a.inv_tau, -mx) - lsum;
+      a.q[(size_t)r * K + k] = expf(lq);
+      a.lq[(size_t)r * K + k] = lq;
       a.zg[(size_t)r * K + k] = 0.f;
       const int id = a.topk_idx[t * K + k];
       s_ids[wave][k] = (id >= 0 && id < a.V) ? id : INT_MAX;
     }
-    cacc = wave_sum(cacc);
-    if (lane == 0) a.cterm[r] = cacc;
   }
   __syncthreads();
   if (active) {
@@ -113,15 +110,21 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
   }
 }
 
-// Per slice row, after the logits GEMM:
-//  lse_t = logsumexp over segments of (shift_j + log sum_j);
-//  KL_t  = c_t + lse_t - sum_k q_k z_k / tau      (z_k gathered by the GEMM);
-//  P[t, id_k] -= q_k exp(lse_t - shift_j)          (teacher correction, so
-//        that f_j * P is exactly tau/N (p - q_scat) on segment j);
-//  f_j   = tau/N * mask_t * exp(shift_j - lse_t);
+// Per slice row, after the logits GEMM.  Logits are in base-2 units
+// (s2 = log2(e) / tau): shift_j = max over segment j of z s2, sum_j = sum
+// over the segment of 2^(z s2 - shift_j).  With M = max_j shift_j and
+// s = sum_j sum_j 2^(shift_j - M), log2-sum-exp2 of the row is M + log2 s, so
+//  lse   = (M + log2 s) ln 2                      (natural units, z / tau);
+//  KL_t  = sum_k q_k (log q_k - (z_k s2 - M) ln 2) + log s  (z_k gathered by
+//          the GEMM); every bracket is a difference of nearby values taken
+//          with one rounding, so KL_t keeps its accuracy as it tends to 0;
+//  P[t, id_k] = 2^(z_k s2 - shift_j) - q_k 2^(M - shift_j + log2 s), from
+//          the fp32 logit z_k and rounded once (the teacher correction, so
+//          that f_j * P is tau/N (p - q_scat) on segment j);
+//  f_j   = tau/N * mask_t * 2^(shift_j - M - log2 s);
 //  G[t, v] = f_seg(v) * P[t, v]  written over P (= tau/N mask (p - q_scat)).
 // A segment holding teacher ids whose shift lies more than RESHIFT_NATS
-// below lse_t is first re-shifted to lse_t - RESHIFT_NATS.
+// below the row's logsumexp is first re-shifted to RESHIFT_NATS below it.
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -136,24 +139,30 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   for (int j = lane; j < nseg; j += 64) mx = fmaxf(mx, mrow[j]);
   mx = wave_max(mx);
   float s = 0.f;
-  for (int j = lane; j < nseg; j += 64) s += srow[j] * exp2f((mrow[j] - mx) * LOG2E);
+  for (int j = lane; j < nseg; j += 64) s += srow[j] * exp2f(mrow[j] - mx);
   s = wave_sum(s);
-  const float lse = mx + logf(s);
+  const float log2s = log2f(s);
+  const float lse2 = mx + log2s;  // base 2
+  const float lse = lse2 * LN2;
 
+  const float *q = a.q + (size_t)r * K;
+  const float *lq = a.lq + (size_t)r * K;
+  const float *zg = a.zg + (size_t)r * K;
   float dot = 0.f;
-  for (int k = lane; k < K; k += 64) dot += a.q[(size_t)r * K + k] * a.zg[(size_t)r * K + k];
+  for (int k = lane; k < K; k += 64) dot += q[k] * (lq[k] - fmaf(zg[k], a.s2, -mx) * LN2);
   dot = wave_sum(dot);
   const bool valid = a.mask ? (a.mask[t] != 0) : true;
   if (lane == 0) {
     a.lse[r] = lse;
     if (a.lse_out) a.lse_out[t] = lse;
-    a.row_loss[t] = valid ? (a.cterm[r] + lse - dot * a.inv_tau) : 0.f;
+    a.row_loss[t] = valid ? (dot + log2s * LN2) : 0.f;
   }
   if (!a.need_grad) return;
 
   const float gscale = valid ? a.scal->grad_scale : 0.f;
   T *P = reinterpret_cast<T *>(a.P) + (size_t)r * a.ldp;
   const int32_t *sid = a.sid + (size_t)r * K;
+  constexpr float RESHIFT2 = RESHIFT_NATS * LOG2E;
   if (gscale != 0.f) {
     for (int base = 0; base < K; base += 64) {
       const int pos = base + lane;
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
         if (id < a.V) {
           j = id / SEG;
           const bool first_in_seg = pos == 0 || (sid[pos - 1] / SEG) != j;
-          need = first_in_seg && (lse - mrow[j] > RESHIFT_NATS);
+          need = first_in_seg && (lse2 - mrow[j] > RESHIFT2);
         }
       }
       uint64_t bal = __ballot(need);
@@ -172,8 +181,8 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
         const int src = __ffsll((unsigned long long)bal) - 1;
         bal &= bal - 1;
         const int js = __shfl(j, src, 64);
-        const float newm = lse - RESHIFT_NATS;
-        const float fac = exp2f((mrow[js] - newm) * LOG2E);
+        const float newm = lse2 - RESHIFT2;
+        const float fac = exp2f(mrow[js] - newm);
         for (int c = lane; c < SEG; c += 64) {
           T &e = P[(size_t)js * SEG + c];
           e = Elem<T>::from_f(Elem<T>::to_f(e) * fac);
@@ -189,14 +198,16 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
       if (id < a.V) {
         const int j = id / SEG;
         const int slot = a.sslot[(size_t)r * K + pos];
-        const float corr = a.q[(size_t)r * K + slot] * exp2f((lse - mrow[j]) * LOG2E);
-        P[id] = Elem<T>::from_f(Elem<T>::to_f(P[id]) - corr);
+        const float mj = mrow[j];
+        const float pz = exp2f(fmaf(zg[slot], a.s2, -mj));
+        const float corr = q[slot] * exp2f((mx - mj) + log2s);
+        P[id] = Elem<T>::from_f(pz - corr);
       }
     }
   }
   float *frow = a.fseg + (size_t)r * nseg;
   for (int j = lane; j < nseg; j += 64)
-    frow[j] = gscale != 0.f ? gscale * exp2f((mrow[j] - lse) * LOG2E) : 0.f;
+    frow[j] = gscale != 0.f ? gscale * exp2f((mrow[j] - mx) - log2s) : 0.f;
   if (a.fast) return;  // k_scale_g forms G (and G^T) on the tuned path
   __threadfence_block();
   // G row = f_seg * P row, in place: the logit gradient the dH and dW GEMMs

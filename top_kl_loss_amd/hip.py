@@ -1,10 +1,10 @@
-"""Minimal ctypes access to the HIP runtime that libkdtopk.so runs on.
+"""Minimal ctypes access to the HIP runtime of the process.
 
-PyTorch-ROCm ships its own HIP runtime, so a process that uses both torch
-and libkdtopk.so holds two runtime instances: device memory is shared, but
-streams and events of one are unknown to the other.  Work of the library is
-therefore ordered against torch's by host synchronisation (see the binding),
-and timed with events of the library's own runtime (this module).
+The binding loads libkdtopk.so after torch, so the library, torch and this
+module all use the one runtime torch loaded (soname libamdhip64.so.7).  The
+benchmark uses it for what torch does not expose: events recorded by the
+library's launch log around single kernel launches, device attributes and
+hipMemGetInfo.
 """
 from __future__ import annotations
 
@@ -14,12 +14,12 @@ _hip = None
 
 
 def runtime():
-    """The HIP runtime instance libkdtopk.so is linked against."""
+    """The HIP runtime of the process (the one torch and libkdtopk.so use)."""
     global _hip
     if _hip is not None:
         return _hip
     from . import load_library
-    load_library()  # makes sure the library's runtime is the loaded one
+    load_library()  # loads torch's runtime first, then the library
     h = ctypes.CDLL("libamdhip64.so.7")
     vp = ctypes.c_void_p
     h.hipDeviceSynchronize.restype = ctypes.c_int
@@ -69,7 +69,7 @@ def set_device(index: int):
 
 
 def synchronize(stream=None):
-    """Wait for `stream` of the library's runtime (None: whole device)."""
+    """Wait for `stream` (a raw handle; None: the whole device)."""
     if stream is None:
         check(runtime().hipDeviceSynchronize())
     else:
@@ -77,7 +77,8 @@ def synchronize(stream=None):
 
 
 class Stream:
-    """A default-priority stream of the library's runtime."""
+    """A default-priority stream created through the runtime (raw handle in
+    ``value``; torch.cuda.ExternalStream can wrap it)."""
 
     def __init__(self):
         self.handle = ctypes.c_void_p()
@@ -96,7 +97,7 @@ class Stream:
 
 
 class Event:
-    """A timing event of the library's runtime."""
+    """A timing event (raw handle in ``value``), for the launch log."""
 
     def __init__(self):
         self.handle = ctypes.c_void_p()
