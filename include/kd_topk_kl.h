@@ -30,8 +30,9 @@
  * ---------------------------------
  * - All tensors are dense, row-major, contiguous, in device memory of the
  *   current HIP device; the caller allocates and owns every buffer.  The
- *   library allocates nothing and keeps no state between calls (apart from
- *   the optional, per-thread measurement hook kd_set_launch_log).
+ *   library allocates nothing and keeps no state between calls, apart from
+ *   the optional, per-thread measurement hook kd_set_launch_log and the
+ *   fixed per-GPU scratch of kd_topk_kl_fwd_noalloc.
  * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *   the default stream).  Outputs are valid once that stream has
  *   synchronised.  No call synchronises the host.
@@ -61,7 +62,9 @@ enum {
   KD_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required    */
   KD_ERR_UNSUPPORTED = 3, /* valid but unsupported: d % 8 != 0, K > KD_MAX_K,
                              sizes beyond 32-bit index range, unknown dtype */
-  KD_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
+  KD_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed     */
+  KD_ERR_SCRATCH = 5      /* kd_topk_kl_fwd_noalloc: the sizes need more than
+                             KD_NOALLOC_SCRATCH_BYTES of scratch            */
 };
 
 /* Flags for kd_topk_kl_fwd_bwd. */
@@ -154,6 +157,36 @@ int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
                    int32_t K, float tau, int32_t chunk, float *loss,
                    float *row_loss, float *lse, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* Bytes of device scratch kd_topk_kl_fwd_noalloc holds per GPU. */
+#define KD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kd_topk_kl_fwd_noalloc -- kd_topk_kl_fwd for callers that cannot allocate
+ * device memory at call time (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): it takes no workspace and calls
+ * no allocating routine.  Its scratch is a fixed device array of
+ * KD_NOALLOC_SCRATCH_BYTES per GPU, set up by the runtime when the library
+ * is loaded and held until the process ends; its address on a device is
+ * looked up once, on the first call made with that device current.
+ *
+ * Arguments, outputs and results as for kd_topk_kl_fwd (the same kernels:
+ * loss, row_loss and lse are bitwise those of kd_topk_kl_fwd for the same
+ * chunk).  The scratch needs, with C = min(chunk, T) and nseg = ceil(V/256),
+ *     at most 4 T + C (20 K + 10 nseg + 4) + 3072 bytes
+ * (about 10 MB for T = 32768, V = 201088, K = 100, chunk = 1024); larger
+ * problems are rejected with KD_ERR_SCRATCH before any HIP call.  Nothing in
+ * the scratch needs to be zero on entry (every call writes what it reads).
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (two streams, two threads) race and give undefined results; calls on
+ * different GPUs do not interact.  Returns KD_OK, KD_ERR_INVALID_ARG,
+ * KD_ERR_UNSUPPORTED, KD_ERR_SCRATCH or KD_ERR_HIP.
+ */
+int kd_topk_kl_fwd_noalloc(const void *H, const void *W, kd_dtype dtype,
+                           const int32_t *topk_idx, const float *topk_logit,
+                           const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                           int32_t K, float tau, int32_t chunk, float *loss,
+                           float *row_loss, float *lse, void *stream);
 
 /*
  * kd_topk_kl_bwd -- dH and dW of grad_loss * loss, recomputing the logits

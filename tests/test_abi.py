@@ -1,7 +1,6 @@
 """Host-side tests of the C ABI: the library loads, exports every symbol the
 header declares, sizes its workspace, and rejects bad arguments before any
 HIP call (so these run without a GPU)."""
-import ctypes
 import os
 import re
 
@@ -28,16 +27,16 @@ def test_header_declares_every_exported_entry_point():
 
 
 def test_library_exports_every_declared_symbol():
-    lib = ctypes.CDLL(kd.LIB_PATH)
+    lib = kd.load_library()      # torch's HIP runtime first, then the library
     for name in declared_functions():
         assert hasattr(lib, name), name
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert kd.kd_status_string(s).startswith(
             ["KD_OK", "KD_ERR_INVALID_ARG", "KD_ERR_WORKSPACE",
-             "KD_ERR_UNSUPPORTED", "KD_ERR_HIP"][s])
+             "KD_ERR_UNSUPPORTED", "KD_ERR_HIP", "KD_ERR_SCRATCH"][s])
     assert kd.kd_status_string(99) == "unknown kd status"
 
 
@@ -263,3 +262,45 @@ def test_entropy_filter_workspace_size():
     assert kd.kd_entropy_filter_workspace_size(32768) == 256 + 32768 * 4
     with pytest.raises(kd.KdError):
         kd.kd_entropy_filter_workspace_size(0)
+
+
+def _fwd_noalloc_call(**kw):
+    lib = kd.load_library()
+    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=1, row_loss=None,
+             lse=None, stream=None)
+    a.update(kw)
+    return lib.kd_topk_kl_fwd_noalloc(
+        a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
+        a["d"], a["V"], a["K"], a["tau"], a["chunk"], a["loss"], a["row_loss"],
+        a["lse"], a["stream"])
+
+
+def _noalloc_bytes(T, V, K, chunk):
+    """The header's bound on the allocation-free forward's scratch."""
+    C = min(chunk, T)
+    nseg = (V + 255) // 256
+    return 4 * T + C * (20 * K + 10 * nseg + 4) + 3072
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=None), kd.KD_ERR_INVALID_ARG),
+    (dict(loss=None), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=-1.0), kd.KD_ERR_INVALID_ARG),
+    (dict(T=0), kd.KD_ERR_INVALID_ARG),
+    (dict(d=12), kd.KD_ERR_UNSUPPORTED),
+    # beyond the fixed scratch: the benchmark's slice of 8192 rows at
+    # V = 201088 needs ~81 MB; a 64 MiB scratch takes at most ~6600 rows
+    (dict(T=32768, d=2880, V=201088, chunk=8192), kd.KD_ERR_SCRATCH),
+    (dict(T=1 << 24, d=64, V=256, K=1, chunk=1), kd.KD_ERR_SCRATCH),
+])
+def test_fwd_noalloc_rejects_before_any_hip_call(kw, code):
+    assert _fwd_noalloc_call(**kw) == code
+
+
+def test_fwd_noalloc_scratch_bound_covers_the_benchmark_sizes():
+    # what the header promises fits: T = 32768, V = 201088, K = 100 at
+    # slices up to 4096 rows, and the bound's own arithmetic
+    assert _noalloc_bytes(32768, 201088, 100, 1024) < 11 * 10 ** 6
+    assert _noalloc_bytes(32768, 201088, 100, 4096) < kd.KD_NOALLOC_SCRATCH_BYTES
+    assert _noalloc_bytes(32768, 201088, 100, 8192) > kd.KD_NOALLOC_SCRATCH_BYTES

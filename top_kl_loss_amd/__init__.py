@@ -25,22 +25,26 @@ __all__ = [
     "kd_teacher_topk_workspace_size", "kd_teacher_topk", "kd_topk_kl_fwd",
     "kd_topk_kl_bwd", "kd_grad_cast", "kd_entropy_filter",
     "kd_entropy_filter_workspace_size", "KD_FILTER_ENTROPY_ABOVE",
-    "KD_FILTER_TOP_ENTROPY_FRACTION",
+    "KD_FILTER_TOP_ENTROPY_FRACTION", "kd_topk_kl_fwd_noalloc",
+    "KD_NOALLOC_SCRATCH_BYTES", "KD_ERR_SCRATCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
 
 KD_F32, KD_BF16 = 0, 1
-KD_OK, KD_ERR_INVALID_ARG, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP = range(5)
+(KD_OK, KD_ERR_INVALID_ARG, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP,
+ KD_ERR_SCRATCH) = range(6)
 KD_FLAG_ACCUMULATE_DW = 1
 KD_MAX_K = 1024
 KD_TOPK_MAX_K = 256
 KD_TOPK_MAX_D = 16384
+KD_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log",
                     "kd_teacher_topk_workspace_size", "kd_teacher_topk",
                     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast",
-                    "kd_entropy_filter_workspace_size", "kd_entropy_filter")
+                    "kd_entropy_filter_workspace_size", "kd_entropy_filter",
+                    "kd_topk_kl_fwd_noalloc")
 KD_FILTER_ENTROPY_ABOVE, KD_FILTER_TOP_ENTROPY_FRACTION = 0, 1
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
@@ -96,6 +100,11 @@ def load_library(path: str = LIB_PATH):
         c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
         c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
     lib.kd_topk_kl_fwd.restype = c.c_int
+    lib.kd_topk_kl_fwd_noalloc.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
+        c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+    lib.kd_topk_kl_fwd_noalloc.restype = c.c_int
     lib.kd_topk_kl_bwd.argtypes = [
         c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
         c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
@@ -332,6 +341,36 @@ def kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
             loss.data_ptr(), _ptr(rl), _ptr(ls), workspace.data_ptr(),
             workspace.numel(), call.handle))
     return loss, rl, ls
+
+
+def kd_topk_kl_fwd_noalloc(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                           chunk=None, *, loss=None, row_loss=None, lse=None,
+                           stream=None, sync=False):
+    """kd_topk_kl_fwd without a workspace: the library's fixed per-GPU
+    scratch (KD_NOALLOC_SCRATCH_BYTES) holds the intermediates, so the C call
+    allocates nothing (for code under graph capture or other callers that
+    cannot allocate).  ``loss`` ([1] fp32), ``row_loss`` and ``lse`` ([T]
+    fp32) are output tensors to fill; ``loss`` None is allocated here, and
+    ``row_loss`` / ``lse`` None are not produced.  A bool mask is converted
+    (which allocates); pass uint8 to avoid it.  Calls that overlap on one GPU
+    share the scratch and race.  Returns (loss, row_loss, lse)."""
+    import torch
+    lib = load_library()
+    T, d, V, K, chunk, dt = _loss_inputs(H, W, topk_idx, topk_logit, mask, chunk)
+    dev = H.device
+    for name, t, n in (("loss", loss, 1), ("row_loss", row_loss, T), ("lse", lse, T)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != n
+                              or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous float32 [{n}] tensor on H's device")
+    with _Call(dev, stream, sync) as call:
+        mask = _mask_u8(mask)
+        if loss is None:
+            loss = torch.empty(1, dtype=torch.float32, device=dev)
+        _check(lib.kd_topk_kl_fwd_noalloc(
+            H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+            topk_logit.data_ptr(), _ptr(mask), T, d, V, K, float(tau), chunk,
+            loss.data_ptr(), _ptr(row_loss), _ptr(lse), call.handle))
+    return loss, row_loss, lse
 
 
 def kd_topk_kl_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kd_internal.h"
 #include "kd_topk_kl.h"
 
@@ -71,8 +73,11 @@ int check_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   return KD_OK;
 }
 
+// fwd_only: the regions the forward alone touches (no probabilities, G,
+// gradient factors, dH partials or transposed copies): the compact layout of
+// the allocation-free forward entry point.
 Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
-                   kd_dtype dtype) {
+                   kd_dtype dtype, bool fwd_only = false) {
   Layout L{};
   L.C = (int)(chunk < T ? chunk : T);
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
@@ -99,14 +104,15 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_first = take(sizeof(int16_t) * C * nseg);
   L.o_mseg = take(sizeof(float) * C * nseg);
   L.o_sseg = take(sizeof(float) * C * nseg);
-  L.o_fseg = take(sizeof(float) * C * nseg);
+  const size_t g = fwd_only ? 0 : 1;  // gradient-only regions
+  L.o_fseg = take(g * sizeof(float) * C * nseg);
   L.o_lse = take(sizeof(float) * C);
-  L.o_P = take(L.esize * C * (size_t)L.ldp);
-  L.o_dhp = take(sizeof(float) * (size_t)L.splits * C * (size_t)d);
+  L.o_P = take(g * L.esize * C * (size_t)L.ldp);
+  L.o_dhp = take(g * sizeof(float) * (size_t)L.splits * C * (size_t)d);
   L.ldh = (int)((C + 63) / 64 * 64);
-  L.o_ht = take(L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0);
-  L.o_gt = take(L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0);
-  L.o_wt = take(L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0);
+  L.o_ht = take(g * (L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0));
+  L.o_gt = take(g * (L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0));
+  L.o_wt = take(g * (L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0));
   L.total = o;
   return L;
 }
@@ -191,12 +197,12 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
              int64_t T, int64_t d, int64_t V, int32_t K, float tau, int32_t chunk,
              uint32_t flags, const float *grad_loss, float *loss, float *row_loss,
              float *lse_out, float *dH, float *dW, void *workspace,
-             size_t workspace_bytes, void *stream) {
+             size_t workspace_bytes, void *stream, bool compact = false) {
   if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
   if (flags & ~uint32_t(KD_FLAG_ACCUMULATE_DW)) return KD_ERR_INVALID_ARG;
   const int st = check_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
-  const Layout L = make_layout(T, d, V, K, chunk, dtype);
+  const Layout L = make_layout(T, d, V, K, chunk, dtype, compact && mode == MODE_FWD);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return KD_ERR_WORKSPACE;
@@ -311,6 +317,69 @@ int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
   return run_loss(MODE_FWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
                   tau, chunk, 0u, nullptr, loss, row_loss, lse, nullptr, nullptr,
                   workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device scratch of kd_topk_kl_fwd_noalloc: one array per GPU, allocated by
+// the runtime when the library's code object is loaded and kept until the
+// process ends.  Host code never uses the array's name as an address (it is
+// a host-side stand-in); each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int KD_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[KD_MAX_DEVICES] = {};
+
+// The current device's address of `scratch` (nullptr and the HIP error on
+// failure).
+void *scratch_ptr(hipError_t *err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= KD_MAX_DEVICES)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_kl_fwd_noalloc(const void *H, const void *W, kd_dtype dtype,
+                           const int32_t *topk_idx, const float *topk_logit,
+                           const uint8_t *mask, int64_t T, int64_t d, int64_t V,
+                           int32_t K, float tau, int32_t chunk, float *loss,
+                           float *row_loss, float *lse, void *stream) {
+  if (!H || !W || !topk_idx || !topk_logit || !loss) return KD_ERR_INVALID_ARG;
+  if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  // the size check runs before any HIP call
+  if (make_layout(T, d, V, K, chunk, dtype, true).total > KD_NOALLOC_SCRATCH_BYTES)
+    return KD_ERR_SCRATCH;
+  hipError_t e = hipSuccess;
+  void *ws = scratch_ptr(&e);
+  if (!ws) return hip_fail(e);
+  return run_loss(MODE_FWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
+                  tau, chunk, 0u, nullptr, loss, row_loss, lse, nullptr, nullptr,
+                  ws, KD_NOALLOC_SCRATCH_BYTES, stream, /*compact=*/true);
 }
 
 int kd_topk_kl_bwd(const void *H, const void *W, kd_dtype dtype,
@@ -472,6 +541,10 @@ const char *kd_status_string(int status) {
       return "KD_ERR_UNSUPPORTED: d % 8 != 0, K > KD_MAX_K, unknown dtype or "
              "sizes beyond the 32-bit index range";
     case KD_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "KD_ERR_HIP: HIP error";
+    case KD_ERR_SCRATCH:
+      return "KD_ERR_SCRATCH: the forward's scratch for these sizes and this "
+             "chunk exceeds the fixed KD_NOALLOC_SCRATCH_BYTES of "
+             "kd_topk_kl_fwd_noalloc (use a smaller chunk)";
     default: return "unknown kd status";
   }
 }
