@@ -46,7 +46,7 @@ TRAFFIC_KERNELS = {
     "loss": [("k_fast_logits(", "gemm_logits", _GEMM_SRC),
              ("k_fast_dh", "gemm_dh", _GEMM_SRC),
              ("k_fast_dw", "gemm_dw", _GEMM_SRC),
-             ("k_scale_g(", "scale_g", _GEMM_SRC),
+             ("k_fast_logits_redo(", "flagged_rows", _GEMM_SRC),
              ("k_transpose_w(", "transpose_w", _GEMM_SRC),
              ("k_transpose_h(", "transpose_h", _GEMM_SRC),
              ("k_lse_fix<", "lse_fix", _ROW_SRC),

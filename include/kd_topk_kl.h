@@ -271,7 +271,8 @@ enum {
   KD_KERNEL_GEMM_DW = 6,     /* dW (+)= G^T H_c                              */
   KD_KERNEL_FINAL_LOSS = 7,  /* loss = tau^2/N sum_t row_loss                */
   KD_KERNEL_TRANSPOSE_H = 8, /* H_c^T staging for the dW GEMM (bf16 path)    */
-  KD_KERNEL_SCALE_G = 9,     /* G = f P in place and G^T (bf16 path)         */
+  KD_KERNEL_FLAGGED_ROWS = 9, /* bf16 path: rows whose a-priori shift was too
+                                low, recomputed with the row maximum         */
   KD_KERNEL_TRANSPOSE_W = 10, /* W^T once per call (bf16 path, chunk >= d)   */
   /* kd_teacher_topk */
   KD_KERNEL_TK_SAMPLE = 11,  /* logits of the sampled vocabulary segments    */

@@ -52,7 +52,8 @@ struct Layout {
   bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_lq, o_zg, o_sid, o_sslot, o_first,
-      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt;
+      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt, o_shift,
+      o_frow, o_flag, o_tflag;
   bool wt;
   int dh_bn, dw_bn;
   int ldh;
@@ -113,6 +114,10 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_ht = take(g * (L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0));
   L.o_gt = take(g * (L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0));
   L.o_wt = take(g * (L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0));
+  L.o_shift = take(g * sizeof(float) * C);
+  L.o_frow = take(g * sizeof(float) * C);
+  L.o_flag = take(g * sizeof(int32_t) * C);
+  L.o_tflag = take(g * sizeof(int32_t) * ((C + kd::ROW_TILE - 1) / kd::ROW_TILE));
   L.total = o;
   return L;
 }
@@ -243,6 +248,10 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
   a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
   a.Ht = reinterpret_cast<uint16_t *>(ws + L.o_ht);
   a.Gt = reinterpret_cast<uint16_t *>(ws + L.o_gt);
+  a.shift = reinterpret_cast<float *>(ws + L.o_shift);
+  a.frow = reinterpret_cast<float *>(ws + L.o_frow);
+  a.flag = reinterpret_cast<int32_t *>(ws + L.o_flag);
+  a.tile_flags = reinterpret_cast<int32_t *>(ws + L.o_tflag);
   a.Wt = (L.wt && grads) ? reinterpret_cast<uint16_t *>(ws + L.o_wt) : nullptr;
   a.ldh = L.ldh;
   a.dh_stride = (size_t)L.C * (size_t)d;
@@ -274,7 +283,7 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
         (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })))
       return hip_fail(e);
     if (!grads) continue;
-    if ((a.fast && (e = logged(KD_KERNEL_SCALE_G, s, [&] { return kd::launch_scale_g(a, s); }))) ||
+    if ((a.fast && (e = logged(KD_KERNEL_FLAGGED_ROWS, s, [&] { return kd::launch_flagged_rows(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
         (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))) ||

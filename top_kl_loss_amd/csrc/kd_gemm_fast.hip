@@ -4,9 +4,13 @@
 //
 //  logits:  Z = H_c W^T      (C x V, K = d)   + softmax-statistics epilogue
 //  dH:      dH_c = G W       (C x d, K = V)   split-K over the vocabulary
-//  dW:      dW (+)= G^T H_c  (V x d, K = C)   operands G^T and H_c^T
-// G is the slice's logit gradient: k_scale_g writes it in bf16 over the P
-// buffer and also writes G^T; k_transpose_h writes H_c^T.
+//  dW:      dW (+)= G^T H_c  (V x d, K = C)   operands P~^T and (f H_c)^T
+// The logits GEMM stores the slice's probabilities P~ = 2^(z s2 - sh_t) with
+// one a-priori shift per row, in bf16, row-major and transposed; k_lse_fix
+// applies the teacher correction at the ids and the per-row gradient factor
+// f_t, so that G = f_t P~.  dH = f_t (P~ W) (the factor applied when the
+// split-K partials are reduced) and dW = P~^T (f H_c) (k_transpose_h writes
+// (f H_c)^T).
 //
 // The tile machinery (4-wave and 8-wave tiles, DMA operand copies, swizzled
 // LDS layouts, MFMA schedules) is in kd_mfma_tile.h.
@@ -23,27 +27,43 @@ namespace {
 using namespace tile;
 
 // ------------------------------------------------------------ logits GEMM
-// A = H_c, B = W (both K-contiguous), 4-wave tiles.  Epilogue per row and
-// segment, in base-2 units (s2 = log2(e) / tau): the shift max(z) s2,
-// P = 2^(z s2 - shift) in bf16, the sum of P, and z itself at the row's
-// teacher ids inside the segment (the student-logit gather).
-__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_fast_logits(SliceArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+// A = H_c, B = W (both K-contiguous), 4-wave tiles, one 256 x 256 tile
+// (rows m0.., vocabulary segment seg) per call.  Units are base 2
+// (s2 = log2(e) / tau).
+//  MODE 0, per row and segment: the shift max(z) s2 and the sum of
+//    2^(z s2 - shift) (the softmax statistics), z itself at the row's teacher
+//    ids inside the segment (the student-logit gather), and, when gradients
+//    are wanted, the probabilities with the row's a-priori shift sh_t,
+//    P~ = 2^(z s2 - sh_t), stored in bf16 twice: row-major [C, ldp] (the dH
+//    operand) and transposed [ldp, ldh] (the dW operand, tokens contiguous),
+//    the latter from a transposed copy in LDS so that every store writes
+//    whole 128-byte lines.  Rows at or past C are stored as 0 in P~^T.
+//  MODE 1: the same logits, stored only for the rows flagged by k_lse_fix,
+//    with their exact maximum as shift (no statistics, no gather).
+// The wave tiles interleave their 16-row blocks (w4::SquareI: block i of
+// wave row wm holds tile rows 32 i + 16 wm ..), so the epilogue runs in 4
+// passes of 64 consecutive tile rows staged by all four waves: pass p stages
+// blocks 2p and 2p + 1 of both wave rows, and stage row sr is tile row
+// 64 p + sr.  Thread (pr, part) = (tid / 8, tid % 8) takes the two rows
+// 2 pr and 2 pr + 1 and the 8-column groups part, part + 8, ... of them, so
+// the 8 threads of a row store whole lines of P~ and each thread packs the
+// pair of adjacent tokens of a column into one word of the transposed copy
+// (word (col, pr) at col * 32 + 4 ((pr >> 2) ^ ((col >> 3) & 7)) + (pr & 3):
+// 16-byte chunks XOR-swizzled per column).
+template <int MODE>
+__device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg, char *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nmt = (a.C + BM - 1) / BM;
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  int mt, seg;
-  group_tile(tile, nmt, a.nseg, 4, mt, seg);
   const int m0 = mt * BM, n0 = seg * SEG;
   const uint16_t *H = reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d;
   const uint16_t *W = reinterpret_cast<const uint16_t *>(a.W);
-  using S = w4::Square;
+  using S = w4::SquareI;
   w4::Copy<S::RA> ca;
   w4::Copy<S::RB> cb;
   ca.init(H, (uint64_t)a.C * a.d * 2, a.d, m0, wave, lane);
   cb.init(W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
+  const bool grads = MODE == 1 || a.need_grad;
+  const int part = tid & 7, pr = tid >> 3;
 
   // Teacher ids of tile row m0 + tid inside this segment, fetched now so
   // that their latency hides under the main loop: up to NHIT (column, slot)
@@ -53,7 +73,7 @@ void k_fast_logits(SliceArgs a) {
   bool more = false;
 #pragma unroll
   for (int q = 0; q < NHIT; ++q) hit_col[q] = -1;
-  if (m0 + tid < a.C) {
+  if (MODE == 0 && m0 + tid < a.C) {
     const int r = m0 + tid;
     const int pos = a.first[(size_t)r * a.nseg + seg];
     if (pos >= 0) {
@@ -71,22 +91,28 @@ void k_fast_logits(SliceArgs a) {
       if (pos + NHIT < a.K && sid[pos + NHIT] < n0 + SEG) more = true;
     }
   }
+  // Shifts of this thread's 8 rows (2 per pass); rows past C store 0
+  // (shift +inf).  MODE 1: only flagged rows are stored (others +inf too).
+  float sh[4][2];
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = m0 + 64 * pass + 2 * pr + q;
+      sh[pass][q] = INFINITY;
+      if (grads && r < a.C && (MODE == 0 || a.flag[r])) sh[pass][q] = a.shift[r];
+    }
 
   f32x4 acc[8][8];
   w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
   __syncthreads();
 
-  // Epilogue in 4 passes; pass p stages block-rows 2p and 2p + 1 of both
-  // wave rows: 64 tile rows x 256 columns, tile row
-  // wm * 128 + (2p + ii) * 16 + r at stage row wm * 32 + ii * 16 + r.  Each
-  // row is processed by TPR threads, and each thread takes RPT rows at once
-  // (independent work to overlap with one wave per SIMD).
   constexpr int PITCH = BN + 4;
-  constexpr int SROWS = 64, TPR = 8, RPT = SROWS * TPR / w4::NT, CPT = BN / TPR;
+  constexpr int TPR = 8, CPT = BN / TPR;
   float *stage = reinterpret_cast<float *>(lds);
+  uint32_t *tb = reinterpret_cast<uint32_t *>(lds + 64 * PITCH * 4);
   uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
-  const int part = tid % TPR;
   const float s2 = a.s2;
   const bool tail = n0 + BN > a.V;
 #pragma unroll
@@ -97,67 +123,80 @@ void k_fast_logits(SliceArgs a) {
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          stage[(wm * 32 + ii * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
+          stage[(ii * 32 + wm * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
                 w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
-    // Thread `part` of a row owns the 8-column groups part, part + 8, ...,
-    // so the row's TPR threads store whole 128-byte lines of P together
-    // (contiguous 64-byte runs per thread would split every line).
-    // Base-2 units: shift = max(z) s2 (s2 = log2(e) / tau) and
-    // P = 2^(z s2 - shift) with the exponent rounded once (fma), so P keeps
-    // its relative accuracy however large z s2 is; only the vocabulary's
-    // last segment has columns past V (excluded).
-    float v[RPT][CPT];
-    float mx[RPT], sum[RPT];
+    // z of the thread's two rows (-inf past V: only the vocabulary's last
+    // segment has such columns)
+    float v[2][CPT];
 #pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-      const int sr = tid / TPR + q * (w4::NT / TPR);
-      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int j = 0; j < CPT / 8; ++j) {
-        const int col = j * 8 * TPR + part * 8;
+      for (int j = 0; j < CPT / 8; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + sr * PITCH + col + 4 * h);
+          const int col = j * 8 * TPR + part * 8 + 4 * h;
+          const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + (2 * pr + q) * PITCH + col);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int c = j * 8 + 4 * h + u;
-            v[q][c] = z[u];
-            if (tail && n0 + col + 4 * h + u >= a.V) v[q][c] = -INFINITY;
-            m4[u] = fmaxf(m4[u], v[q][c]);
-          }
+          for (int u = 0; u < 4; ++u)
+            v[q][j * 8 + 4 * h + u] = (tail && n0 + col + u >= a.V) ? -INFINITY : z[u];
         }
+    const int r0 = m0 + 64 * pass + 2 * pr;
+    if (MODE == 0) {
+      float mx[2], sum[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) m4[c & 3] = fmaxf(m4[c & 3], v[q][c]);
+        mx[q] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
       }
-      mx[q] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    }
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1)
+      for (int o = 1; o < TPR; o <<= 1)
 #pragma unroll
-      for (int q = 0; q < RPT; ++q) mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
+        for (int q = 0; q < 2; ++q) mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
 #pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-      mx[q] *= s2;  // the segment's shift, base-2 units
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 2; ++q) {
+        mx[q] *= s2;  // the segment's shift, base-2 units
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        // P~ = 2^(z s2 - mx) 2^(mx - sh): one scale per row and segment
+        const float cq = __builtin_amdgcn_exp2f(mx[q] - sh[pass][q]);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        // 2^(-inf) = 0 covers the excluded columns
-        const float pv = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -mx[q]));
-        v[q][c] = pv;
-        s4[c & 3] += pv;
+        for (int c = 0; c < CPT; ++c) {
+          // 2^(-inf) = 0 covers the excluded columns
+          const float pv = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -mx[q]));
+          s4[c & 3] += pv;
+          v[q][c] = pv * cq;
+        }
+        sum[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       }
-      sum[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) sum[q] += __shfl_xor(sum[q], o, 64);
+      if (part == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (r0 + q < a.C) {
+            a.mseg[(size_t)(r0 + q) * a.nseg + seg] = mx[q];
+            a.sseg[(size_t)(r0 + q) * a.nseg + seg] = sum[q];
+          }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+          v[q][c] = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -sh[pass][q]));
     }
+    if (grads) {
+      // rows past C (and, in MODE 1, rows not flagged) hold +inf shifts:
+      // their P~ is 0, stored only into the transposed copy in MODE 0
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1)
-#pragma unroll
-      for (int q = 0; q < RPT; ++q) sum[q] += __shfl_xor(sum[q], o, 64);
-#pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-      const int sr = tid / TPR + q * (w4::NT / TPR);
-      const int r = m0 + (sr >> 5) * 128 + (2 * pass + ((sr >> 4) & 1)) * 16 + (sr & 15);
-      if (r < a.C) {
-        uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
-        if (a.need_grad) {
+      for (int q = 0; q < 2; ++q) {
+        const int r = r0 + q;
+        if (r < a.C && (MODE == 0 || sh[pass][q] != INFINITY)) {
+          uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
 #pragma unroll
           for (int j = 0; j < CPT / 8; ++j) {
             const int c = j * 8;
@@ -165,18 +204,30 @@ void k_fast_logits(SliceArgs a) {
                     pack_bf16x2(v[q][c + 4], v[q][c + 5]), pack_bf16x2(v[q][c + 6], v[q][c + 7])};
             *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) = w;
           }
+          if (MODE == 1) {
+            // flagged rows are rare: their transposed entries one by one
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+              const int col = (c >> 3) * 8 * TPR + part * 8 + (c & 7);
+              a.Gt[(size_t)(n0 + col) * a.ldh + r] = uint16_t(f32_to_bf16_rne(v[q][c]));
+            }
+          }
         }
-        if (part == 0) {
-          a.mseg[(size_t)r * a.nseg + seg] = mx[q];
-          a.sseg[(size_t)r * a.nseg + seg] = sum[q];
+      }
+      if (MODE == 0) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int col = (c >> 3) * 8 * TPR + part * 8 + (c & 7);
+          tb[col * 32 + (((pr >> 2) ^ ((col >> 3) & 7)) << 2) + (pr & 3)] =
+              pack_bf16x2(v[0][c], v[1][c]);
         }
       }
     }
     // Gather z at the teacher ids: thread tid owns tile row tid, staged in
-    // pass (tid & 127) >> 5 at stage row (tid >> 7) * 32 + (tid & 31).
-    if (((tid & 127) >> 5) == pass) {
+    // pass tid >> 6 at stage row tid & 63.
+    if (MODE == 0 && (tid >> 6) == pass) {
       const int r_own = m0 + tid;
-      const int sr_own = (tid >> 7) * 32 + (tid & 31);
+      const int sr_own = tid & 63;
       if (r_own < a.C) {
         float *zg = a.zg + (size_t)r_own * a.K;
 #pragma unroll
@@ -193,6 +244,42 @@ void k_fast_logits(SliceArgs a) {
         }
       }
     }
+    __syncthreads();
+    // P~^T rows n0 .. n0 + 255, tokens m0 + 64 pass .. + 63: 16 bytes (8
+    // tokens) per thread and column, 8 threads per 128-byte line
+    if (MODE == 0 && grads && m0 + 64 * pass < a.ldh) {
+      const int g = tid & 7;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int col = (tid >> 3) + 32 * i;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(tb + col * 32 + ((g ^ ((col >> 3) & 7)) << 2));
+        *reinterpret_cast<u32x4 *>(a.Gt + (size_t)(n0 + col) * a.ldh + m0 + 64 * pass + 8 * g) = w;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fast_logits(SliceArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nmt = (a.C + BM - 1) / BM;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  int mt, seg;
+  group_tile(tile, nmt, a.nseg, 4, mt, seg);
+  logits_tile<0>(a, mt, seg, lds);
+}
+
+// Rows flagged by k_lse_fix: one workgroup per vocabulary segment walks the
+// slice's M-tiles and recomputes those holding flagged rows (none: a few
+// flag reads and no other work).
+__global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fast_logits_redo(SliceArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nmt = (a.C + BM - 1) / BM;
+  const int seg = xcd_swizzle(blockIdx.x, gridDim.x);
+  for (int mt = 0; mt < nmt; ++mt) {
+    if (a.tile_flags[mt] == 0) continue;
+    logits_tile<1>(a, mt, seg, lds);
     __syncthreads();
   }
 }
@@ -336,12 +423,14 @@ void k_fast_dw4(SliceArgs a) {
     }
 }
 
-// dst[j * ldd + r] = src[r * d + j] for r < nrows, 0 for nrows <= r < ldd
+// dst[j * ldd + r] = src[r * d + j] (times rscale[r] when rscale is not
+// null, rounded to nearest even) for r < nrows, 0 for nrows <= r < ldd
 // (bf16, d and ldd multiples of 64), over 64 (r) x 64 (j) tiles: 16-byte
 // loads of the source rows, a transposing read from LDS, 16-byte stores of
 // the destination rows.  256 threads.
 __device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, int64_t d, int nrows,
-                                            uint16_t *__restrict__ dst, int64_t ldd) {
+                                            uint16_t *__restrict__ dst, int64_t ldd,
+                                            const float *__restrict__ rscale = nullptr) {
   // pitch 66 elements: the column reads of 8 rows 8 apart hit 8 banks
   __shared__ uint16_t t_s[64][66];
   const int r0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
@@ -350,7 +439,10 @@ __device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, in
   for (int h = 0; h < 2; ++h) {
     const int rr = (tid >> 3) + 32 * h;
     u32x4 v{0u, 0u, 0u, 0u};
-    if (r0 + rr < nrows) v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + rr) * d + j0 + ch * 8);
+    if (r0 + rr < nrows) {
+      v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + rr) * d + j0 + ch * 8);
+      if (rscale) v = Elem<uint16_t>::scale(v, rscale[r0 + rr]);
+    }
     uint32_t *row = reinterpret_cast<uint32_t *>(&t_s[rr][0]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) row[ch * 4 + q] = v[q];
@@ -369,49 +461,17 @@ __device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, in
   }
 }
 
-// H_c^T [d, ldh] per slice (token columns t >= C zero).
+// (f H_c)^T [d, ldh] per slice, each token row scaled by its gradient
+// factor f_t (token columns t >= C zero): with P~^T this gives
+// dW = P~^T (f H_c) = G^T H_c.
 __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
-  transpose64(reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d, a.d, a.C, a.Ht, a.ldh);
+  transpose64(reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d, a.d, a.C, a.Ht, a.ldh,
+              a.frow);
 }
 
 // W^T [d, ldp] once per call (vocabulary columns v >= V zero).
 __global__ __launch_bounds__(256) void k_transpose_w(SliceArgs a) {
   transpose64(reinterpret_cast<const uint16_t *>(a.W), a.d, a.V, a.Wt, a.ldp);
-}
-
-// G = f[t, seg] * P over one 64-row x 256-column (one segment) tile, written
-// in place, and G^T[v, t] through LDS; G^T columns t >= C are zero.
-__global__ __launch_bounds__(256) void k_scale_g(SliceArgs a) {
-  __shared__ uint16_t g_s[64][256 + 8];
-  const int t0 = blockIdx.x * 64, seg = blockIdx.y, v0 = seg * SEG;
-  const int tid = threadIdx.x;
-  uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
-  const int c = tid & 31;            // 16-byte chunk of the 512-byte row
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 5) + 8 * i;
-    const int t = t0 + r;
-    u32x4 v{0u, 0u, 0u, 0u};
-    if (t < a.C) {
-      u32x4 *src = reinterpret_cast<u32x4 *>(P + (size_t)t * a.ldp + v0) + c;
-      v = Elem<uint16_t>::scale(*src, a.fseg[(size_t)t * a.nseg + seg]);
-      __builtin_nontemporal_store(v, src);  // streamed: read once by dH
-    }
-    *reinterpret_cast<u32x4 *>(&g_s[r][c * 8]) = v;
-  }
-  __syncthreads();
-  // G^T rows v0.. of this tile: 64 tokens = 128 bytes each, written by 8
-  // consecutive lanes (16 bytes each) so every store fills whole lines.
-  const int q = tid & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int vr = (tid >> 3) + 32 * i;
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      o[p] = uint32_t(g_s[q * 8 + 2 * p][vr]) | (uint32_t(g_s[q * 8 + 2 * p + 1][vr]) << 16);
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(a.Gt + (size_t)(v0 + vr) * a.ldh + t0) + q);
-  }
 }
 
 template <typename K>
@@ -479,11 +539,11 @@ hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s) {
+hipError_t launch_flagged_rows(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
-  const dim3 g((a.ldh + 63) / 64, a.nseg);
-  hipLaunchKernelGGL(k_scale_g, g, dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = launch(k_fast_logits_redo, a.nseg, a, s, w4::Square::LDS, w4::NT);
+  if (e != hipSuccess) return e;
+  return launch_fix_flagged(a, s);
 }
 
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {

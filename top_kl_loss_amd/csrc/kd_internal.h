@@ -13,11 +13,21 @@ namespace kd {
 // vocabulary entries; the backward GEMMs align their tiles to it.
 constexpr int SEG = 256;
 
-// A segment's stored probabilities are shifted by the segment's own maximum.
-// When the row's logsumexp lies more than this far (in units of z/tau)
-// above a segment maximum that carries teacher ids, the segment is shifted
-// again so that the teacher correction stays finite in the stored type.
+// Generic path: a segment's stored probabilities are shifted by the
+// segment's own maximum.  When the row's logsumexp lies more than this far
+// (in units of z/tau) above a segment maximum that carries teacher ids, the
+// segment is shifted again so that the teacher correction stays finite in
+// the stored type.
 constexpr float RESHIFT_NATS = 60.0f;
+
+// Tuned path: the probabilities of a row are stored as 2^(z s2 - shift) with
+// one a-priori shift per row (the largest student logit among the row's
+// SHIFT_SLOTS best teacher slots, a lower bound of the row maximum).  A row
+// whose maximum lies more than SHIFT_LIMIT2 (base-2 units) above its shift
+// is flagged and its probabilities are recomputed with the exact maximum.
+constexpr int SHIFT_SLOTS = 8;
+constexpr float SHIFT_LIMIT2 = 64.0f;
+constexpr int ROW_TILE = 256;  // rows per M-tile of the tuned logits GEMM
 
 // Device-resident scalars written once per call.
 struct Scalars {
@@ -53,8 +63,12 @@ struct SliceArgs {
   float *mseg;       // [Cmax, nseg] segment max of z s2 (shift, base-2 units)
   float *sseg;       // [Cmax, nseg] segment sum of 2^(z s2 - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
-  uint16_t *Ht;      // [d, ldh] bf16 H_c^T (tuned path only)
-  uint16_t *Gt;      // [ldp, ldh] bf16 G^T (tuned path only)
+  uint16_t *Ht;      // [d, ldh] bf16 (f H_c)^T (tuned path only)
+  uint16_t *Gt;      // [ldp, ldh] bf16 transposed probabilities P^T (tuned)
+  float *shift;      // [Cmax] tuned path: row shift (base-2 units)
+  float *frow;       // [Cmax] tuned path: gradient factor f_t of the row
+  int32_t *flag;     // [Cmax] tuned path: 1 = row recomputed with its max
+  int32_t *tile_flags;  // [ceil(Cmax/ROW_TILE)] flagged rows per M-tile
   uint16_t *Wt;      // [d, ldp] bf16 W^T (tuned path with C >= d), or null
   int ldh;           // row pitch of Ht: Cmax rounded up to 64
   float *lse;        // [Cmax] row logsumexp of z/tau
@@ -94,9 +108,12 @@ hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s);
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s);
 // Tuned path with a W^T buffer: W^T once per call (before the slices).
 hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s);
-// Tuned path: G = f_seg * P in place and G^T (no-op on the generic path,
-// where k_lse_fix scales P itself).
-hipError_t launch_scale_g(const SliceArgs &a, hipStream_t s);
+// Tuned path: rows flagged by k_lse_fix (shift too far below the row
+// maximum) get their probabilities recomputed with the maximum and their
+// teacher correction; no work beyond a flag check when none is flagged.
+hipError_t launch_flagged_rows(const SliceArgs &a, hipStream_t s);
+// The teacher correction of the flagged rows (part of launch_flagged_rows).
+hipError_t launch_fix_flagged(const SliceArgs &a, hipStream_t s);
 
 // Launch wrappers; each returns hipSuccess or the launch error.
 hipError_t launch_valid_count(const uint8_t *mask, int T, float tau,

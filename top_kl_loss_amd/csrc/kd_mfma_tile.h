@@ -258,10 +258,20 @@ __device__ __forceinline__ int swz4(int row) { return (row & 7) ^ ((row >> 3) & 
 
 // Tile of 2 x 2 waves, each TMB x TNB blocks of 16 x 16: A has 32 TMB rows,
 // B 32 TNB rows per stage (128 bytes each).  Every half-step reads
-// TMB + TNB = 16 fragments and issues 16 copy instructions per wave.
-template <int TMB_, int TNB_>
+// TMB + TNB = 16 fragments and issues 16 copy instructions per wave.  With
+// AIL (A interleaved), wave row wm holds the 16-row blocks i of tile rows
+// 32 i + 16 wm .. + 15 instead of 16 TMB wm + 16 i .. + 15, so that any 32
+// consecutive tile rows come from both wave rows (an epilogue can stage
+// contiguous rows with all four waves).
+template <int TMB_, int TNB_, bool AIL_ = false>
 struct Shape {
   static constexpr int TMB = TMB_, TNB = TNB_;
+  static constexpr bool AIL = AIL_;
+  static constexpr int ASTRIDE = AIL ? 4096 : 2048;  // bytes between A blocks
+  // first tile row of A block i of wave row wm
+  __device__ static __forceinline__ int arow(int wm, int i) {
+    return AIL ? 32 * i + 16 * wm : 16 * TMB * wm + 16 * i;
+  }
   static constexpr int RA = 32 * TMB, RB = 32 * TNB;  // operand rows per stage
   static constexpr int OPA = RA * 128;                // B starts here
   static constexpr int STB = (RA + RB) * 128;
@@ -271,6 +281,7 @@ struct Shape {
   static_assert(TMB * TNB * 4 <= 256, "accumulators fit the AGPRs");
 };
 using Square = Shape<8, 8>;   // 256 x 256
+using SquareI = Shape<8, 8, true>;  // 256 x 256, A blocks interleaved
 using Tall = Shape<6, 10>;    // 192 x 320 (N = d multiple of 320)
 static_assert(Tall::LDS <= 160 * 1024, "LDS");
 
@@ -322,14 +333,15 @@ struct FragOff {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = ((4 * h + kq) ^ swz4(r)) << 4;
-      a[h] = (wm * 16 * S::TMB + r) * 128 + c;
+      a[h] = (S::arow(wm, 0) + r) * 128 + c;
       b[h] = S::OPA + (wn * 16 * S::TNB + r) * 128 + c;
     }
   }
 };
 
+template <int STRIDE = 2048>
 __device__ __forceinline__ u32x4 rd(const char *stage, int off, int i) {
-  return *reinterpret_cast<const u32x4 *>(stage + off + i * 2048);
+  return *reinterpret_cast<const u32x4 *>(stage + off + i * STRIDE);
 }
 
 // Fragment r of a half in the order the MFMAs use them: A0, B0.., A1...
@@ -337,11 +349,11 @@ template <class S>
 __device__ __forceinline__ void read_frag(const char *stage, int aoff, int boff, int r,
                                           u32x4 (&fa)[S::TMB], u32x4 (&fb)[S::TNB]) {
   if (r == 0)
-    fa[0] = rd(stage, aoff, 0);
+    fa[0] = rd<S::ASTRIDE>(stage, aoff, 0);
   else if (r <= S::TNB)
     fb[r - 1] = rd(stage, boff, r - 1);
   else
-    fa[r - S::TNB] = rd(stage, aoff, r - S::TNB);
+    fa[r - S::TNB] = rd<S::ASTRIDE>(stage, aoff, r - S::TNB);
 }
 
 // The TMB x TNB MFMAs of one k32 half on (fa, fb), spread over 16 slots; in
@@ -427,7 +439,8 @@ __device__ __forceinline__ void acc_ready(f32x4 (&acc)[TMB][TNB]) {
     for (int j = 0; j < TNB; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-// Position of accumulator element e of block (i, j) in the wave tile.
+// Position of accumulator element e of block (i, j) in the wave tile (rows:
+// of a wave row without AIL; with AIL add 16 wm to arow-based positions).
 __device__ __forceinline__ int acc_row4(int i, int e, int lane) { return i * 16 + 4 * (lane >> 4) + e; }
 __device__ __forceinline__ int acc_col4(int j, int lane) { return j * 16 + (lane & 15); }
 

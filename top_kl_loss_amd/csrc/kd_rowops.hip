@@ -81,6 +81,57 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
       s_ids[wave][k] = (id >= 0 && id < a.V) ? id : INT_MAX;
     }
   }
+  // Tuned path with gradients: the row's a-priori shift, the largest z s2
+  // over its SHIFT_SLOTS best teacher slots (teacher logit descending, equal
+  // logits by slot), from fp32 dot products of the bf16 rows of H and W.
+  // Each is an actual logit of the row up to rounding, so the shift lies at
+  // or below the row maximum; -inf when no slot holds a valid id.
+  if (active && a.fast && a.need_grad) {
+    const float *lg = a.topk_logit + t * K;
+    const int R = K < SHIFT_SLOTS ? K : SHIFT_SLOTS;
+    const int dq = a.d / 8;
+    const u32x4 *h16 = reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const uint16_t *>(a.H) + t * a.d);
+    uint32_t taken = 0;  // bit i: slot lane + 64 i already used
+    float best = -INFINITY;
+    for (int rr = 0; rr < R; ++rr) {
+      float bv = -INFINITY;
+      int bk = INT_MAX;
+      for (int i = 0, k = lane; k < K; ++i, k += 64)
+        if (!((taken >> i) & 1u) && (lg[k] > bv || (lg[k] == bv && k < bk))) {
+          bv = lg[k];
+          bk = k;
+        }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int ok = __shfl_xor(bk, o, 64);
+        if (ov > bv || (ov == bv && ok < bk)) {
+          bv = ov;
+          bk = ok;
+        }
+      }
+      if (bk == INT_MAX) break;
+      if ((bk & 63) == lane) taken |= 1u << (bk >> 6);
+      const int id = a.topk_idx[t * K + bk];
+      if (id < 0 || id >= a.V) continue;
+      const u32x4 *w16 = reinterpret_cast<const u32x4 *>(
+          reinterpret_cast<const uint16_t *>(a.W) + (int64_t)id * a.d);
+      float acc = 0.f;
+      for (int c = lane; c < dq; c += 64) {
+        const u32x4 hv = h16[c], wv = w16[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = fmaf(bf16_hi(hv[e]), bf16_hi(wv[e]), fmaf(bf16_lo(hv[e]), bf16_lo(wv[e]), acc));
+      }
+      best = fmaxf(best, wave_sum(acc));
+    }
+    if (lane == 0) {
+      a.shift[r] = best * a.s2;
+      a.flag[r] = 0;
+      if (r % ROW_TILE == 0) a.tile_flags[r / ROW_TILE] = 0;
+    }
+  }
   __syncthreads();
   if (active) {
     for (int k = lane; k < K; k += 64) {
@@ -110,6 +161,43 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
   }
 }
 
+// Row statistics from the logits GEMM's per-segment shifts and sums (base-2
+// units): M = max_j shift_j and s = sum_j sum_j 2^(shift_j - M), so that
+// log2-sum-exp2 of the row is M + log2 s.  Wave-uniform results.
+__device__ __forceinline__ void row_stats(const SliceArgs &a, int r, int lane, float &mx,
+                                          float &log2s) {
+  const float *mrow = a.mseg + (size_t)r * a.nseg;
+  const float *srow = a.sseg + (size_t)r * a.nseg;
+  mx = -INFINITY;
+  for (int j = lane; j < a.nseg; j += 64) mx = fmaxf(mx, mrow[j]);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int j = lane; j < a.nseg; j += 64) s += srow[j] * exp2f(mrow[j] - mx);
+  log2s = log2f(wave_sum(s));
+}
+
+// Tuned path: the teacher correction of row r with the row's shift sh, in
+// both stored layouts: at every valid teacher id,
+//   P~[r, id] = P~^T[id, r] = 2^(z_k s2 - sh) - q_k 2^(M + log2 s - sh),
+// from the fp32 logit z_k, rounded once to bf16.
+__device__ __forceinline__ void correct_rows_tuned(const SliceArgs &a, int r, int lane, float sh,
+                                                   float mx, float log2s) {
+  const int K = a.K;
+  const int64_t t = a.c0 + r;
+  const float *q = a.q + (size_t)r * K;
+  const float *zg = a.zg + (size_t)r * K;
+  uint16_t *P = reinterpret_cast<uint16_t *>(a.P) + (size_t)r * a.ldp;
+  const float corr = exp2f((mx - sh) + log2s);
+  for (int k = lane; k < K; k += 64) {
+    const int id = a.topk_idx[t * K + k];
+    if (id < 0 || id >= a.V) continue;
+    const float val = exp2f(fmaf(zg[k], a.s2, -sh)) - q[k] * corr;
+    const uint16_t b = uint16_t(f32_to_bf16_rne(val));
+    P[id] = b;
+    a.Gt[(size_t)id * a.ldh + r] = b;
+  }
+}
+
 // Per slice row, after the logits GEMM.  Logits are in base-2 units
 // (s2 = log2(e) / tau): shift_j = max over segment j of z s2, sum_j = sum
 // over the segment of 2^(z s2 - shift_j).  With M = max_j shift_j and
@@ -133,15 +221,9 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   const int nseg = a.nseg, K = a.K;
   const int64_t t = a.c0 + r;
   float *mrow = a.mseg + (size_t)r * nseg;
-  const float *srow = a.sseg + (size_t)r * nseg;
 
-  float mx = -INFINITY;
-  for (int j = lane; j < nseg; j += 64) mx = fmaxf(mx, mrow[j]);
-  mx = wave_max(mx);
-  float s = 0.f;
-  for (int j = lane; j < nseg; j += 64) s += srow[j] * exp2f(mrow[j] - mx);
-  s = wave_sum(s);
-  const float log2s = log2f(s);
+  float mx, log2s;
+  row_stats(a, r, lane, mx, log2s);
   const float lse2 = mx + log2s;  // base 2
   const float lse = lse2 * LN2;
 
@@ -160,6 +242,27 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   if (!a.need_grad) return;
 
   const float gscale = valid ? a.scal->grad_scale : 0.f;
+  if (a.fast) {
+    // Tuned path: the GEMM stored P~ = 2^(z s2 - sh) with the row's
+    // a-priori shift sh, so G = f_t P~ (after the teacher correction) with
+    // one factor per row, f_t = tau/N mask 2^(sh - M - log2 s).  A shift
+    // more than SHIFT_LIMIT2 below the row maximum (P~ may have overflowed)
+    // flags the row: its shift becomes the maximum, and k_fast_logits_redo
+    // and k_fix_flagged store it again.
+    float sh = a.shift[r];
+    const bool flagged = !(mx - sh <= SHIFT_LIMIT2);
+    if (flagged) sh = mx;
+    if (lane == 0) {
+      a.frow[r] = gscale != 0.f ? gscale * exp2f((sh - mx) - log2s) : 0.f;
+      if (flagged) {
+        a.shift[r] = sh;
+        a.flag[r] = 1;
+        atomicAdd(&a.tile_flags[r / ROW_TILE], 1);
+      }
+    }
+    if (!flagged && gscale != 0.f) correct_rows_tuned(a, r, lane, sh, mx, log2s);
+    return;
+  }
   T *P = reinterpret_cast<T *>(a.P) + (size_t)r * a.ldp;
   const int32_t *sid = a.sid + (size_t)r * K;
   constexpr float RESHIFT2 = RESHIFT_NATS * LOG2E;
@@ -208,7 +311,6 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
   float *frow = a.fseg + (size_t)r * nseg;
   for (int j = lane; j < nseg; j += 64)
     frow[j] = gscale != 0.f ? gscale * exp2f((mrow[j] - mx) - log2s) : 0.f;
-  if (a.fast) return;  // k_scale_g forms G (and G^T) on the tuned path
   __threadfence_block();
   // G row = f_seg * P row, in place: the logit gradient the dH and dW GEMMs
   // consume (all zero for a padding row).
@@ -219,6 +321,19 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
     const float f = frow[(c * E) / SEG];
     P16[c] = Elem<T>::scale(P16[c], f);
   }
+}
+
+// Tuned path, after k_fast_logits_redo: the teacher correction of the
+// flagged rows (shift = row maximum), in both stored layouts.
+__global__ __launch_bounds__(256) void k_fix_flagged(SliceArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * ROWS_PER_WG + wave;
+  if (r >= a.C || !a.flag[r]) return;
+  const bool valid = a.mask ? (a.mask[a.c0 + r] != 0) : true;
+  if (!valid || a.scal->grad_scale == 0.f) return;
+  float mx, log2s;
+  row_stats(a, r, lane, mx, log2s);
+  correct_rows_tuned(a, r, lane, a.shift[r], mx, log2s);
 }
 
 // dst[i] = src[i] * (*scale) (scale null: 1) in the destination type (bf16
@@ -233,15 +348,18 @@ __global__ __launch_bounds__(256) void k_grad_cast(const float *src, T *dst, int
     dst[i] = Elem<T>::from_f(src[i] * s);
 }
 
-// dH rows of the slice = ordered sum of the split-K partials.
+// dH rows of the slice = ordered sum of the split-K partials, times the
+// row's gradient factor on the tuned path (frow; null on the generic path,
+// whose G carries its factors already).
 __global__ __launch_bounds__(256) void k_reduce_dh(const float *part, int splits,
-                                                   size_t stride, size_t n4,
-                                                   float *out) {
+                                                   size_t stride, size_t n4, int d4,
+                                                   const float *frow, float *out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   f32x4 acc = reinterpret_cast<const f32x4 *>(part)[i];
   for (int s = 1; s < splits; ++s)
     acc += reinterpret_cast<const f32x4 *>(part + s * stride)[i];
+  if (frow) acc *= frow[i / d4];
   reinterpret_cast<f32x4 *>(out)[i] = acc;
 }
 
@@ -305,7 +423,8 @@ hipError_t launch_reduce_dh(const SliceArgs &a, hipStream_t s) {
   const size_t n4 = (size_t)a.C * a.d / 4;
   const int g = (int)((n4 + 255) / 256);
   hipLaunchKernelGGL(k_reduce_dh, dim3(g), dim3(256), 0, s, a.dh_part, a.splits,
-                     a.dh_stride, n4, a.dH + a.c0 * a.d);
+                     a.dh_stride, n4, a.d / 4, a.fast ? a.frow : nullptr,
+                     a.dH + a.c0 * a.d);
   return hipGetLastError();
 }
 
@@ -315,4 +434,12 @@ hipError_t launch_final_loss(const float *row_loss, int T, const Scalars *scal,
   return hipGetLastError();
 }
 
+}  // namespace kd
+
+namespace kd {
+hipError_t launch_fix_flagged(const SliceArgs &a, hipStream_t s) {
+  const int g = (a.C + ROWS_PER_WG - 1) / ROWS_PER_WG;
+  hipLaunchKernelGGL(k_fix_flagged, dim3(g), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 }  // namespace kd
