@@ -91,8 +91,12 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
       if (pos + NHIT < a.K && sid[pos + NHIT] < n0 + SEG) more = true;
     }
   }
-  // Shifts of this thread's 8 rows (2 per pass); rows past C store 0
-  // (shift +inf).  MODE 1: only flagged rows are stored (others +inf too).
+  f32x4 acc[8][8];
+  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
+
+  // Shifts of this thread's 8 rows (2 per pass), loaded after the main loop
+  // (registers there are full); rows past C store 0 (shift +inf).  MODE 1:
+  // only flagged rows are stored (others +inf too).
   float sh[4][2];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass)
@@ -102,9 +106,6 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
       sh[pass][q] = INFINITY;
       if (grads && r < a.C && (MODE == 0 || a.flag[r])) sh[pass][q] = a.shift[r];
     }
-
-  f32x4 acc[8][8];
-  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
   __syncthreads();
 
@@ -126,11 +127,14 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
           stage[(ii * 32 + wm * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
                 w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
-    // z of the thread's two rows (-inf past V: only the vocabulary's last
-    // segment has such columns)
-    float v[2][CPT];
+    // Rows one at a time (fewer live registers): z of the row (-inf past V:
+    // only the vocabulary's last segment has such columns), the statistics,
+    // and P~ packed to bf16 pairs of adjacent columns, pk[q][c / 2].
+    const int r0 = m0 + 64 * pass + 2 * pr;
+    uint32_t pk[2][CPT / 2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 2; ++q) {
+      float v[CPT];
 #pragma unroll
       for (int j = 0; j < CPT / 8; ++j)
 #pragma unroll
@@ -139,94 +143,81 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
           const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + (2 * pr + q) * PITCH + col);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            v[q][j * 8 + 4 * h + u] = (tail && n0 + col + u >= a.V) ? -INFINITY : z[u];
+            v[j * 8 + 4 * h + u] = (tail && n0 + col + u >= a.V) ? -INFINITY : z[u];
         }
-    const int r0 = m0 + 64 * pass + 2 * pr;
-    if (MODE == 0) {
-      float mx[2], sum[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      if (MODE == 0) {
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) m4[c & 3] = fmaxf(m4[c & 3], v[q][c]);
-        mx[q] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-      }
+        for (int c = 0; c < CPT; ++c) m4[c & 3] = fmaxf(m4[c & 3], v[c]);
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        mx[q] *= s2;  // the segment's shift, base-2 units
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        mx *= s2;  // the segment's shift, base-2 units
         // P~ = 2^(z s2 - mx) 2^(mx - sh): one scale per row and segment
-        const float cq = __builtin_amdgcn_exp2f(mx[q] - sh[pass][q]);
+        const float cq = __builtin_amdgcn_exp2f(mx - sh[pass][q]);
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
           // 2^(-inf) = 0 covers the excluded columns
-          const float pv = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -mx[q]));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(v[c], s2, -mx));
           s4[c & 3] += pv;
-          v[q][c] = pv * cq;
+          v[c] = pv * cq;
         }
-        sum[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        if (part == 0 && r0 + q < a.C) {
+          a.mseg[(size_t)(r0 + q) * a.nseg + seg] = mx;
+          a.sseg[(size_t)(r0 + q) * a.nseg + seg] = sum;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) v[c] = __builtin_amdgcn_exp2f(fmaf(v[c], s2, -sh[pass][q]));
       }
+      if (grads) {
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) sum[q] += __shfl_xor(sum[q], o, 64);
-      if (part == 0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          if (r0 + q < a.C) {
-            a.mseg[(size_t)(r0 + q) * a.nseg + seg] = mx[q];
-            a.sseg[(size_t)(r0 + q) * a.nseg + seg] = sum[q];
-          }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int c = 0; c < CPT; ++c)
-          v[q][c] = __builtin_amdgcn_exp2f(fmaf(v[q][c], s2, -sh[pass][q]));
-    }
-    if (grads) {
-      // rows past C (and, in MODE 1, rows not flagged) hold +inf shifts:
-      // their P~ is 0, stored only into the transposed copy in MODE 0
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
+        for (int c = 0; c < CPT; c += 2) pk[q][c / 2] = pack_bf16x2(v[c], v[c + 1]);
+        // rows past C (and, in MODE 1, rows not flagged) hold +inf shifts:
+        // their P~ is 0, stored only into the transposed copy in MODE 0
         const int r = r0 + q;
         if (r < a.C && (MODE == 0 || sh[pass][q] != INFINITY)) {
           uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
 #pragma unroll
-          for (int j = 0; j < CPT / 8; ++j) {
-            const int c = j * 8;
-            u32x4 w{pack_bf16x2(v[q][c], v[q][c + 1]), pack_bf16x2(v[q][c + 2], v[q][c + 3]),
-                    pack_bf16x2(v[q][c + 4], v[q][c + 5]), pack_bf16x2(v[q][c + 6], v[q][c + 7])};
-            *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) = w;
-          }
+          for (int j = 0; j < CPT / 8; ++j)
+            *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) =
+                u32x4{pk[q][4 * j], pk[q][4 * j + 1], pk[q][4 * j + 2], pk[q][4 * j + 3]};
           if (MODE == 1) {
             // flagged rows are rare: their transposed entries one by one
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
               const int col = (c >> 3) * 8 * TPR + part * 8 + (c & 7);
-              a.Gt[(size_t)(n0 + col) * a.ldh + r] = uint16_t(f32_to_bf16_rne(v[q][c]));
+              a.Gt[(size_t)(n0 + col) * a.ldh + r] =
+                  uint16_t((c & 1) ? pk[q][c / 2] >> 16 : pk[q][c / 2] & 0xffffu);
             }
           }
         }
       }
-      if (MODE == 0) {
+    }
+    if (MODE == 0 && grads) {
+      // the token pair (2 pr, 2 pr + 1) of each column: one word of the
+      // transposed copy; (col >> 3) & 7 == part for all of this thread's
+      // columns, so the chunk is (pr >> 2) ^ part
+      uint32_t *tw = tb + part * 8 * 32 + ((((pr >> 2) ^ part) << 2) + (pr & 3));
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int col = (c >> 3) * 8 * TPR + part * 8 + (c & 7);
-          tb[col * 32 + (((pr >> 2) ^ ((col >> 3) & 7)) << 2) + (pr & 3)] =
-              pack_bf16x2(v[0][c], v[1][c]);
-        }
+      for (int c = 0; c < CPT; c += 2) {
+        const int col0 = (c >> 3) * 8 * TPR + (c & 7);  // minus part * 8
+        tw[col0 * 32] = __builtin_amdgcn_perm(pk[1][c / 2], pk[0][c / 2], 0x05040100u);
+        tw[(col0 + 1) * 32] = __builtin_amdgcn_perm(pk[1][c / 2], pk[0][c / 2], 0x07060302u);
       }
     }
     // Gather z at the teacher ids: thread tid owns tile row tid, staged in
     // pass tid >> 6 at stage row tid & 63.
     if (MODE == 0 && (tid >> 6) == pass) {
-      const int r_own = m0 + tid;
+      // the row index is hidden from the compiler here so that it computes
+      // these pointers anew instead of keeping the prologue's across the
+      // main loop
+      int r_own = m0 + tid;
+      asm volatile("" : "+v"(r_own));
       const int sr_own = tid & 63;
       if (r_own < a.C) {
         float *zg = a.zg + (size_t)r_own * a.K;
