@@ -15,5 +15,6 @@ from .kd_oracle import (  # noqa: F401
     slice_terms,
     teacher_distribution,
     teacher_entropy,
+    topk_divergence,
 )
 from .teacher_topk import teacher_logits, teacher_topk_cache  # noqa: F401

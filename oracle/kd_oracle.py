@@ -56,6 +56,7 @@ import numpy as np
 __all__ = [
     "teacher_entropy",
     "entropy_filter_mask",
+    "topk_divergence",
     "teacher_distribution",
     "log_softmax_rows",
     "kd_topk_kl",
@@ -319,3 +320,69 @@ def entropy_filter_mask(topk_logit, mask, tau, mode, param):
     out = np.zeros(T, dtype=np.uint8)
     out[kept] = 1
     return out
+
+
+def topk_divergence(H, W, topk_idx, topk_logit, mask, tau, kind):
+    """Reverse KL or Jensen-Shannon divergence over the teacher's top-K
+    support, with analytic gradients (readings D1-D3).
+
+    The asibiont.com article (section "A Concrete Implementation Sketch")
+    distils with a KL divergence between the softened distributions; the
+    question the pages leave open is whether the cached top-K keeps enough
+    signal ("Hugging Face and Multiverse Computing cut KD memory costs",
+    agent-gateway.com, closing paragraph).  Over the same cache:
+
+    * D1  both distributions live on the row's K cached ids: the teacher
+          q = softmax(topk_logit / tau) (as R1) and the student restricted to
+          those ids and renormalised, p^ = softmax(z[t, idx] / tau);
+    * D2  kind "reverse_kl": D_t = sum_k p^_k (log p^_k - log q_k);
+          kind "jsd": with m = (p^ + q) / 2,
+          D_t = 1/2 sum_k q_k log(q_k / m_k) + 1/2 sum_k p^_k log(p^_k / m_k);
+    * D3  loss = tau^2 / N * sum_t mask_t D_t as R3 (N = 0: zeros).
+
+    Gradient (derived): with u = z[t, idx] / tau and a_k = dD/dp^_k,
+    a = log(p^/q) + 1 (reverse KL) or a = 1/2 log(p^/m) (JSD), the softmax
+    Jacobian gives dD/du_k = p^_k (a_k - sum_j p^_j a_j); the loss gradient
+    tau / N * mask_t * that lands on the K ids only.  Then dH = G W and
+    dW = G^T H with G the dense [T, V] gradient (zero off the ids).
+    Inputs are upcast exactly to fp64.  Returns loss, row_loss (mask * D_t),
+    dH, dW and n_valid.
+    """
+    if kind not in ("reverse_kl", "jsd"):
+        raise ValueError(kind)
+    H = _f64(H)
+    W = _f64(W)
+    ids = np.asarray(topk_idx, dtype=np.int64)
+    T, d = H.shape
+    V = W.shape[0]
+    tau = float(tau)
+    m = _mask_vector(mask, T)
+    n_valid = float(m.sum())
+    q, log_q = teacher_distribution(topk_logit, tau)              # D1, teacher
+    z = H @ W.T
+    u = np.take_along_axis(z, ids, axis=1) / tau
+    log_p, _ = log_softmax_rows(u)                               # D1, student
+    p = np.exp(log_p)
+    if kind == "reverse_kl":
+        div = (p * (log_p - log_q)).sum(axis=1)
+        a = log_p - log_q + 1.0
+    else:
+        log_mid = np.log(0.5 * (p + q))
+        div = 0.5 * (q * (log_q - log_mid)).sum(axis=1) + \
+            0.5 * (p * (log_p - log_mid)).sum(axis=1)
+        a = 0.5 * (log_p - log_mid)
+    du = p * (a - (p * a).sum(axis=1, keepdims=True))
+    grad_scale = tau / n_valid if n_valid > 0 else 0.0
+    loss_scale = tau * tau / n_valid if n_valid > 0 else 0.0
+    Gk = du * (grad_scale * m)[:, None]                          # dL/dz at the ids
+    G = np.zeros((T, V))
+    np.add.at(G, (np.repeat(np.arange(T), ids.shape[1]), ids.reshape(-1)),
+              Gk.reshape(-1))
+    row_loss = m * div
+    return {
+        "loss": loss_scale * row_loss.sum(),
+        "row_loss": row_loss,
+        "dH": G @ W,
+        "dW": G.T @ H,
+        "n_valid": n_valid,
+    }
