@@ -210,14 +210,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--op", choices=("loss", "fwd", "bwd", "teacher_topk",
-                                     "entropy_filter"),
+                                     "entropy_filter", "reverse_kl", "jsd"),
                     default="loss",
                     help="loss: kd_topk_kl_fwd_bwd (default); fwd: "
                          "kd_topk_kl_fwd (loss only); bwd: kd_topk_kl_bwd "
                          "(gradients, logits recomputed); teacher_topk: "
                          "kd_teacher_topk, the teacher cache build; "
                          "entropy_filter: kd_entropy_filter (top 70% of "
-                         "tokens by teacher entropy)")
+                         "tokens by teacher entropy); reverse_kl / jsd: "
+                         "kd_topk_div_fwd_bwd, the divergence over the "
+                         "top-K support")
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -248,6 +250,8 @@ def main():
         return bench_teacher(args)
     if args.op == "entropy_filter":
         return bench_filter(args)
+    if args.op in ("reverse_kl", "jsd"):
+        return bench_div(args)
 
     import numpy as np
     import torch
@@ -686,6 +690,127 @@ def bench_filter(args):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
                      "traffic": None, "launch_ms": round(avg, 4)},
     }), flush=True)
+
+
+def cpu_baseline_div(x, kind, target_s):
+    """The divergence oracle, as it stands, on the first R tokens."""
+    from oracle import kd_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) \
+            if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+
+    def run(R):
+        m = None if x.mask is None else x.mask[:R]
+        t0 = time.perf_counter()
+        orc.topk_divergence(x.H[:R], x.W, x.topk_idx[:R], x.topk_logit[:R], m,
+                            x.tau, kind)
+        return time.perf_counter() - t0
+
+    t8 = run(8)
+    t32 = run(32)
+    per = max((t32 - t8) / 24, 1e-6)
+    fixed = max(t8 - 8 * per, 0.0)
+    R = int(max(32, min(x.T, 2048, (target_s - fixed) / per)))
+    log(f"cpu baseline: divergence oracle on {R} tokens (~{fixed + per * R:.0f} s)")
+    dt = run(R)
+    model, affinity = cpu_info()
+    return {"value": R / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": model, "affinity_cpus": affinity,
+            "sample": f"first {R} of {x.T} tokens of {x.name} (full d={x.d}, "
+                      f"V={x.V}, K={x.K}), fp64 NumPy (dense logits); "
+                      f"{dt:.1f} s wall"}
+
+
+def bench_div(args):
+    """One step = one kd_topk_div_fwd_bwd call (reverse KL or JSD over the
+    top-K support: loss, dH and dW) over the workload's whole batch."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+
+    torch.cuda.init()
+    lib = kd.load_library()
+    x = synth.workload(args.workload, teacher_device="cuda")
+    T, d, V, K = x.T, x.d, x.V, x.K
+    dev = torch.device("cuda:0")
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        dt_code, esize = kd.KD_BF16, 2
+    else:
+        H = torch.from_numpy(x.H).to(dev)
+        W = torch.from_numpy(x.W).to(dev)
+        dt_code, esize = kd.KD_F32, 4
+    idx = torch.from_numpy(x.topk_idx).to(dev)
+    lg = torch.from_numpy(x.topk_logit).to(dev)
+    mask = None if x.mask is None else torch.from_numpy(x.mask).to(dev)
+    ws_bytes = kd.kd_topk_div_workspace_size(T, d, V, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss, rl = torch.empty(1, **f32), torch.empty(T, **f32)
+    dH, dW = torch.empty(T, d, **f32), torch.empty(V, d, **f32)
+    code = kd.DIVERGENCES[args.op]
+    torch.cuda.synchronize()
+    stream = hip.Stream()
+
+    def step():
+        st = lib.kd_topk_div_fwd_bwd(
+            code, H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+            None if mask is None else mask.data_ptr(), T, d, V, K, float(x.tau), 0,
+            loss.data_ptr(), rl.data_ptr(), dH.data_ptr(), dW.data_ptr(),
+            ws.data_ptr(), ws_bytes, stream.value)
+        if st != 0:
+            raise RuntimeError(kd.kd_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+    cap = args.steps
+    starts = [hip.Event() for _ in range(cap)]
+    ends = [hip.Event() for _ in range(cap)]
+    arr_s = (ctypes.c_void_p * cap)(*[e.value for e in starts])
+    arr_e = (ctypes.c_void_p * cap)(*[e.value for e in ends])
+    count = ctypes.c_int32(0)
+    kd.kd_set_launch_log(1 << 18, arr_s, arr_e, None, cap, ctypes.byref(count))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stream.synchronize()
+    wall = time.perf_counter() - t0
+    kd.kd_set_launch_log(0, None, None, None, 0, None)
+    call_ms = [starts[i].elapsed_ms(ends[i]) for i in range(count.value)]
+    avg = sum(call_ms) / len(call_ms)
+    # algorithmic bytes: H, W and the cache read once, dH and dW written once
+    nbytes = (T + V) * d * esize + T * K * 8 + (T + V) * d * 4
+    gathered = 3 * T * K * d * esize
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    metric = (f"tokens/s {'reverse KL' if args.op == 'reverse_kl' else 'Jensen-Shannon'} "
+              f"over the top-{K} support, fwd+bwd (kd_topk_div_fwd_bwd)")
+    out = {
+        "metric": metric, "value": round(T * args.steps / wall, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": x.dtype, "data": "synthetic",
+        "config": {"workload": x.name, "T": T, "d": d, "V": V, "K": K, "tau": x.tau,
+                   "masked": 0 if x.mask is None else int(T - x.mask.sum()),
+                   "parallelism": "single GPU"},
+        "loss": float(loss.item()),
+        "extra_hbm_bytes": ws_bytes,
+        "roofline": {"bound": "hbm", "kernel": "divergence (all kernels of the call)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_ms": round(avg, 4), "algorithmic_bytes": nbytes,
+                     "gathered_row_bytes": gathered},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_div(x, args.op, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -281,8 +281,63 @@ enum {
   KD_KERNEL_TK_SELECT = 14,  /* exact top-K of each row's candidates         */
   KD_KERNEL_TK_STREAM = 15,  /* row-streaming top-K (generic path, overflow) */
   KD_KERNEL_GRAD_CAST = 16,  /* kd_grad_cast                                 */
-  KD_KERNEL_ENTROPY_FILTER = 17 /* kd_entropy_filter (all of its kernels)    */
+  KD_KERNEL_ENTROPY_FILTER = 17, /* kd_entropy_filter (all of its kernels)   */
+  KD_KERNEL_DIVERGENCE = 18  /* kd_topk_div_fwd_bwd (all kernels but the
+                                final loss sum)                             */
 };
+
+/* Divergences of kd_topk_div_fwd_bwd. */
+enum {
+  KD_DIV_REVERSE_KL = 1, /* KL(p^ || q)                                       */
+  KD_DIV_JSD = 2         /* (KL(q || m) + KL(p^ || m)) / 2, m = (p^ + q) / 2  */
+};
+
+/*
+ * kd_topk_div_workspace_size -- bytes of device scratch kd_topk_div_fwd_bwd
+ * needs: the logit gradient at the ids and the sorted (id, pair) lists,
+ * O(T K + V) words, plus partial dW rows for ids with more than 1024 pairs
+ * (at most 2 ceil(T K / 1024) rows of d floats).  `bytes_out` is a host
+ * pointer.  Returns KD_OK, KD_ERR_INVALID_ARG or KD_ERR_UNSUPPORTED.
+ */
+int kd_topk_div_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                               size_t *bytes_out);
+
+/*
+ * kd_topk_div_fwd_bwd -- loss, dH and dW of a divergence between teacher
+ * and student over the teacher's cached top-K support: the loss variants
+ * that the open question of "Hugging Face and Multiverse Computing cut KD
+ * memory costs" (agent-gateway.com, closing paragraph: how much signal the
+ * top-K cache keeps) calls for, next to the forward KL of kd_topk_kl_fwd_bwd
+ * (the asibiont.com article, section "A Concrete Implementation Sketch",
+ * distils with a divergence between the softened distributions).
+ *
+ * Both distributions live on row t's K cached ids: the teacher
+ * q = softmax(topk_logit[t,:] / tau) and the student restricted to the ids
+ * and renormalised, p^ = softmax(z[t, topk_idx[t,:]] / tau), z = H W^T:
+ *   kind KD_DIV_REVERSE_KL  D_t = sum_k p^_k (log p^_k - log q_k)
+ *   kind KD_DIV_JSD         D_t = 1/2 sum_k q_k log(q_k / m_k)
+ *                                 + 1/2 sum_k p^_k log(p^_k / m_k)
+ *   loss = tau^2 / N * sum_t mask[t] D_t    (0 when N = 0)
+ * The logit gradient is non-zero at the K ids only, so dH and dW come from
+ * gathers of K rows of W and H per token: no [T, V] or chunk x V buffer and
+ * no dense GEMM (O(T K d) work).
+ *
+ * Arguments as for kd_topk_kl_fwd_bwd (no chunk: nothing of size V is
+ * formed per token).  dH [T, d] is overwritten; dW [V, d] is overwritten,
+ * or accumulated into with KD_FLAG_ACCUMULATE_DW (rows of ids no token
+ * references get 0, or keep their value).  Ids outside [0, V) are never
+ * dereferenced.  Sums are ordered (the (id, token) pairs are sorted with a
+ * stable radix sort), so repeated calls give bitwise-identical results.
+ * Returns KD_OK, KD_ERR_INVALID_ARG (unknown kind, NULL pointer, bad sizes
+ * or tau), KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE or KD_ERR_HIP.
+ */
+int kd_topk_div_fwd_bwd(int32_t kind, const void *H, const void *W,
+                        kd_dtype dtype, const int32_t *topk_idx,
+                        const float *topk_logit, const uint8_t *mask,
+                        int64_t T, int64_t d, int64_t V, int32_t K, float tau,
+                        uint32_t flags, float *loss, float *row_loss,
+                        float *dH, float *dW, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* Largest supported K and hidden size of kd_teacher_topk. */
 #define KD_TOPK_MAX_K 256

@@ -304,3 +304,41 @@ def test_fwd_noalloc_scratch_bound_covers_the_benchmark_sizes():
     assert _noalloc_bytes(32768, 201088, 100, 1024) < 11 * 10 ** 6
     assert _noalloc_bytes(32768, 201088, 100, 4096) < kd.KD_NOALLOC_SCRATCH_BYTES
     assert _noalloc_bytes(32768, 201088, 100, 8192) > kd.KD_NOALLOC_SCRATCH_BYTES
+
+
+def _div_call(**kw):
+    lib = kd.load_library()
+    a = dict(kind=kd.KD_DIV_REVERSE_KL, H=1, W=1, dtype=kd.KD_BF16, idx=1,
+             logit=1, mask=None, T=256, d=512, V=8192, K=100, tau=1.0, flags=0,
+             loss=1, row_loss=None, dH=1, dW=1, ws=256, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.kd_topk_div_fwd_bwd(
+        a["kind"], a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"],
+        a["T"], a["d"], a["V"], a["K"], a["tau"], a["flags"], a["loss"],
+        a["row_loss"], a["dH"], a["dW"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=0), kd.KD_ERR_INVALID_ARG),
+    (dict(kind=3), kd.KD_ERR_INVALID_ARG),
+    (dict(H=None), kd.KD_ERR_INVALID_ARG),
+    (dict(dW=None), kd.KD_ERR_INVALID_ARG),
+    (dict(loss=None), kd.KD_ERR_INVALID_ARG),
+    (dict(tau=float("inf")), kd.KD_ERR_INVALID_ARG),
+    (dict(flags=4), kd.KD_ERR_INVALID_ARG),
+    (dict(K=9000), kd.KD_ERR_INVALID_ARG),
+    (dict(d=20), kd.KD_ERR_UNSUPPORTED),
+    (dict(ws=None), kd.KD_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), kd.KD_ERR_WORKSPACE),
+])
+def test_divergence_rejects_before_any_hip_call(kw, code):
+    assert _div_call(**kw) == code
+
+
+def test_divergence_workspace_is_linear_in_pairs_and_vocabulary():
+    a = kd.kd_topk_div_workspace_size(32768, 2880, 201088, 100)
+    b = kd.kd_topk_div_workspace_size(16384, 2880, 201088, 100)
+    dense = 8 * 32768 * 201088
+    assert a < dense / 300                  # ~150 MB against 52.7 GB
+    assert 1.5 * b < a < 2.5 * b            # T K pairs dominate

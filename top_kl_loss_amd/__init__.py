@@ -26,7 +26,8 @@ __all__ = [
     "kd_topk_kl_bwd", "kd_grad_cast", "kd_entropy_filter",
     "kd_entropy_filter_workspace_size", "KD_FILTER_ENTROPY_ABOVE",
     "KD_FILTER_TOP_ENTROPY_FRACTION", "kd_topk_kl_fwd_noalloc",
-    "KD_NOALLOC_SCRATCH_BYTES", "KD_ERR_SCRATCH",
+    "KD_NOALLOC_SCRATCH_BYTES", "KD_ERR_SCRATCH", "KD_DIV_REVERSE_KL",
+    "KD_DIV_JSD", "kd_topk_div_workspace_size", "kd_topk_div_fwd_bwd",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
@@ -39,18 +40,22 @@ KD_MAX_K = 1024
 KD_TOPK_MAX_K = 256
 KD_TOPK_MAX_D = 16384
 KD_NOALLOC_SCRATCH_BYTES = 64 << 20
+KD_DIV_REVERSE_KL, KD_DIV_JSD = 1, 2
+DIVERGENCES = {"reverse_kl": KD_DIV_REVERSE_KL, "jsd": KD_DIV_JSD}
 EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_status_string", "kd_set_launch_log",
                     "kd_teacher_topk_workspace_size", "kd_teacher_topk",
                     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast",
                     "kd_entropy_filter_workspace_size", "kd_entropy_filter",
-                    "kd_topk_kl_fwd_noalloc")
+                    "kd_topk_kl_fwd_noalloc", "kd_topk_div_workspace_size",
+                    "kd_topk_div_fwd_bwd")
 KD_FILTER_ENTROPY_ABOVE, KD_FILTER_TOP_ENTROPY_FRACTION = 0, 1
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
                 "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
                 "flagged_rows", "transpose_w", "tk_sample", "tk_theta", "tk_filter",
-                "tk_select", "tk_stream", "grad_cast", "entropy_filter")
+                "tk_select", "tk_stream", "grad_cast", "entropy_filter",
+                "divergence")
 
 _lib = None
 
@@ -111,6 +116,15 @@ def load_library(path: str = LIB_PATH):
         c.c_uint32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
         c.c_size_t, c.c_void_p]
     lib.kd_topk_kl_bwd.restype = c.c_int
+    lib.kd_topk_div_workspace_size.argtypes = [
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.POINTER(c.c_size_t)]
+    lib.kd_topk_div_workspace_size.restype = c.c_int
+    lib.kd_topk_div_fwd_bwd.argtypes = [
+        c.c_int32, c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p,
+        c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float,
+        c.c_uint32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+        c.c_void_p, c.c_size_t, c.c_void_p]
+    lib.kd_topk_div_fwd_bwd.restype = c.c_int
     lib.kd_grad_cast.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int64,
                                  c.c_void_p, c.c_void_p]
     lib.kd_grad_cast.restype = c.c_int
@@ -405,6 +419,53 @@ def kd_topk_kl_bwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
             int(flags), _ptr(grad_loss), dH.data_ptr(), dW.data_ptr(),
             workspace.data_ptr(), workspace.numel(), call.handle))
     return dH, dW
+
+
+def kd_topk_div_workspace_size(T, d, V, K) -> int:
+    """Workspace bytes for kd_topk_div_fwd_bwd (see the C header)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_topk_div_workspace_size(
+        int(T), int(d), int(V), int(K), ctypes.byref(out)))
+    return out.value
+
+
+def kd_topk_div_fwd_bwd(kind, H, W, topk_idx, topk_logit, mask=None, tau=1.0,
+                        flags=0, *, dW=None, row_loss=True, workspace=None,
+                        stream=None, sync=False):
+    """Reverse KL ("reverse_kl") or Jensen-Shannon ("jsd") divergence over
+    the teacher's top-K support, with dH and dW (see the C header).  Inputs
+    as for kd_topk_kl_fwd_bwd; returns (loss[1], row_loss[T] or None, dH,
+    dW)."""
+    import torch
+    lib = load_library()
+    code = DIVERGENCES.get(kind, kind)
+    if code not in DIVERGENCES.values():
+        raise ValueError(f"kind must be one of {sorted(DIVERGENCES)}")
+    T, d, V, K, _, dt = _loss_inputs(H, W, topk_idx, topk_logit, mask, None)
+    dev = H.device
+    if dW is not None and (dW.shape != (V, d) or dW.dtype != torch.float32
+                           or not dW.is_contiguous() or dW.device != dev):
+        raise ValueError("dW must be float32 [V, d] on H's device")
+    with _Call(dev, stream, sync) as call:
+        mask = _mask_u8(mask)
+        ws_bytes = kd_topk_div_workspace_size(T, d, V, K)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        elif workspace.numel() < ws_bytes:
+            raise ValueError("workspace too small")
+        f32 = dict(dtype=torch.float32, device=dev)
+        loss = torch.empty(1, **f32)
+        rl = torch.empty(T, **f32) if row_loss else None
+        dH = torch.empty(T, d, **f32)
+        if dW is None:
+            dW = torch.empty(V, d, **f32)
+        _check(lib.kd_topk_div_fwd_bwd(
+            int(code), H.data_ptr(), W.data_ptr(), dt, topk_idx.data_ptr(),
+            topk_logit.data_ptr(), _ptr(mask), T, d, V, K, float(tau),
+            int(flags), loss.data_ptr(), _ptr(rl), dH.data_ptr(),
+            dW.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            call.handle))
+    return loss, rl, dH, dW
 
 
 def kd_grad_cast(src, dtype, scale=None, *, out=None, stream=None, sync=False):

@@ -21,8 +21,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (kd_entropy_filter, kd_grad_cast, kd_topk_kl_bwd, kd_topk_kl_fwd,
-               kd_topk_kl_fwd_bwd)
+from . import (kd_entropy_filter, kd_grad_cast, kd_topk_div_fwd_bwd,
+               kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd)
 
 __all__ = ["TopKKLLossFunction", "topk_kl_loss", "TopKKLLoss"]
 
@@ -32,11 +32,20 @@ class TopKKLLossFunction(torch.autograd.Function):
     loss (0-dim fp32); gradients flow to H and W."""
 
     @staticmethod
-    def forward(ctx, H, W, topk_idx, topk_logit, mask, tau, chunk, recompute):
+    def forward(ctx, H, W, topk_idx, topk_logit, mask, tau, chunk, recompute,
+                divergence="forward_kl"):
         ctx.recompute = bool(recompute)
         ctx.tau, ctx.chunk = float(tau), chunk
         ctx.dtypes = (H.dtype, W.dtype)
-        if ctx.recompute:
+        if divergence != "forward_kl":
+            # reverse KL / JSD over the top-K support: one fused call
+            if ctx.recompute:
+                raise ValueError("recompute applies to the forward KL only")
+            loss, _, dH, dW = kd_topk_div_fwd_bwd(divergence, H, W, topk_idx,
+                                                  topk_logit, mask, tau,
+                                                  row_loss=False)
+            ctx.save_for_backward(dH, dW)
+        elif ctx.recompute:
             loss, _, _ = kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask, tau,
                                         chunk, row_loss=False, lse=False)
             ctx.save_for_backward(H, W, topk_idx, topk_logit,
@@ -62,7 +71,7 @@ class TopKKLLossFunction(torch.autograd.Function):
             scale = g
         gH = _finish(dH, ctx.dtypes[0], scale) if ctx.needs_input_grad[0] else None
         gW = _finish(dW, ctx.dtypes[1], scale) if ctx.needs_input_grad[1] else None
-        return gH, gW, None, None, None, None, None, None
+        return gH, gW, None, None, None, None, None, None, None
 
 
 def _finish(g32, dtype, scale):
@@ -74,7 +83,7 @@ def _finish(g32, dtype, scale):
 
 
 def topk_kl_loss(H, W, topk_idx, topk_logit, mask=None, tau=1.0, chunk=None,
-                 recompute=False, entropy_filter=None):
+                 recompute=False, entropy_filter=None, divergence="forward_kl"):
     """tau^2 / N * sum_t mask_t KL(q_t || p_t): the teacher's distribution q
     over its K cached logits against the student's softmax p over all V
     logits z = H W^T, both at temperature tau (see include/kd_topk_kl.h).
@@ -84,23 +93,30 @@ def topk_kl_loss(H, W, topk_idx, topk_logit, mask=None, tau=1.0, chunk=None,
     entropy_filter: None, ("above", threshold) or ("top_fraction", fraction):
     the loss then runs only on the tokens kd_entropy_filter keeps (teacher
     entropy above the threshold, or the given fraction of valid tokens with
-    the highest entropy), and N counts those tokens."""
+    the highest entropy), and N counts those tokens.
+
+    divergence: "forward_kl" (the above), or "reverse_kl" / "jsd": the
+    divergence between the student restricted to the K cached ids
+    (renormalised) and the teacher there (kd_topk_div_fwd_bwd; no chunk)."""
     if entropy_filter is not None:
         mode, param = entropy_filter
         mask, _ = kd_entropy_filter(topk_logit, mask, tau, mode, param,
                                     entropy=False)
     return TopKKLLossFunction.apply(H, W, topk_idx, topk_logit, mask, tau,
-                                    chunk, recompute)
+                                    chunk, recompute, divergence)
 
 
 class TopKKLLoss(torch.nn.Module):
     """Module form of topk_kl_loss with fixed tau, chunk and schedule."""
 
-    def __init__(self, tau=1.0, chunk=None, recompute=False, entropy_filter=None):
+    def __init__(self, tau=1.0, chunk=None, recompute=False, entropy_filter=None,
+                 divergence="forward_kl"):
         super().__init__()
         self.tau, self.chunk, self.recompute = float(tau), chunk, bool(recompute)
         self.entropy_filter = entropy_filter
+        self.divergence = divergence
 
     def forward(self, H, W, topk_idx, topk_logit, mask=None):
         return topk_kl_loss(H, W, topk_idx, topk_logit, mask, self.tau,
-                            self.chunk, self.recompute, self.entropy_filter)
+                            self.chunk, self.recompute, self.entropy_filter,
+                            self.divergence)

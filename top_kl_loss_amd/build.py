@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkdtopk.so")
 SOURCES = ["kd_api.hip", "kd_rowops.hip", "kd_gemm.hip", "kd_gemm_fast.hip",
-           "kd_teacher.hip", "kd_filter.hip"]
+           "kd_teacher.hip", "kd_filter.hip", "kd_div.hip"]
 ARCH = "gfx950"
 
 

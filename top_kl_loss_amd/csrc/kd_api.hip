@@ -477,6 +477,109 @@ int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
   return KD_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct DivLayout {
+  size_t o_scal, o_rowloss, o_gk, o_k0, o_k1, o_v0, o_v1, o_hist, o_seg, o_units, o_parts,
+      o_partial, total;
+};
+
+DivLayout make_div_layout(int64_t T, int64_t d, int64_t V, int32_t K) {
+  DivLayout L{};
+  const size_t n = (size_t)T * K;
+  const size_t nblk = (n + kd::RADIX_BLOCK - 1) / kd::RADIX_BLOCK;
+  const size_t pmax = 2 * ((n + kd::DIV_UNIT - 1) / kd::DIV_UNIT);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  L.o_scal = take(sizeof(kd::Scalars));
+  L.o_rowloss = take(sizeof(float) * (size_t)T);
+  L.o_gk = take(sizeof(float) * n);
+  L.o_k0 = take(sizeof(int32_t) * n);
+  L.o_k1 = take(sizeof(int32_t) * n);
+  L.o_v0 = take(sizeof(int32_t) * n);
+  L.o_v1 = take(sizeof(int32_t) * n);
+  L.o_hist = take(sizeof(int32_t) * 256 * nblk);
+  L.o_seg = take(sizeof(int32_t) * ((size_t)V + 1));
+  L.o_units = take(sizeof(int32_t) * ((size_t)V + 1));
+  L.o_parts = take(sizeof(int32_t) * ((size_t)V + 1));
+  L.o_partial = take(sizeof(float) * pmax * (size_t)d);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_div_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K, size_t *bytes_out) {
+  if (!bytes_out) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, 1, KD_BF16);
+  if (st != KD_OK) return st;
+  *bytes_out = make_div_layout(T, d, V, K).total;
+  return KD_OK;
+}
+
+int kd_topk_div_fwd_bwd(int32_t kind, const void *H, const void *W, kd_dtype dtype,
+                        const int32_t *topk_idx, const float *topk_logit,
+                        const uint8_t *mask, int64_t T, int64_t d, int64_t V, int32_t K,
+                        float tau, uint32_t flags, float *loss, float *row_loss, float *dH,
+                        float *dW, void *workspace, size_t workspace_bytes, void *stream) {
+  if (kind != KD_DIV_REVERSE_KL && kind != KD_DIV_JSD) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW) return KD_ERR_INVALID_ARG;
+  if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
+  if (flags & ~uint32_t(KD_FLAG_ACCUMULATE_DW)) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, 1, dtype);
+  if (st != KD_OK) return st;
+  const DivLayout L = make_div_layout(T, d, V, K);
+  if (!workspace || workspace_bytes < L.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  kd::Scalars *scal = reinterpret_cast<kd::Scalars *>(ws + L.o_scal);
+  float *rl = row_loss ? row_loss : reinterpret_cast<float *>(ws + L.o_rowloss);
+  kd::DivArgs a{};
+  a.H = H;
+  a.W = W;
+  a.topk_idx = topk_idx;
+  a.topk_logit = topk_logit;
+  a.mask = mask;
+  a.scal = scal;
+  a.T = T;
+  a.d = (int)d;
+  a.V = (int)V;
+  a.K = K;
+  a.inv_tau = 1.0f / tau;
+  a.kind = kind;
+  a.bf16 = dtype == KD_BF16 ? 1 : 0;
+  a.accumulate = (flags & KD_FLAG_ACCUMULATE_DW) ? 1 : 0;
+  a.Gk = reinterpret_cast<float *>(ws + L.o_gk);
+  a.row_loss = rl;
+  a.dH = dH;
+  a.dW = dW;
+  a.keys[0] = reinterpret_cast<int32_t *>(ws + L.o_k0);
+  a.keys[1] = reinterpret_cast<int32_t *>(ws + L.o_k1);
+  a.vals[0] = reinterpret_cast<int32_t *>(ws + L.o_v0);
+  a.vals[1] = reinterpret_cast<int32_t *>(ws + L.o_v1);
+  a.hist = reinterpret_cast<int32_t *>(ws + L.o_hist);
+  a.seg = reinterpret_cast<int32_t *>(ws + L.o_seg);
+  a.unit_start = reinterpret_cast<int32_t *>(ws + L.o_units);
+  a.part_start = reinterpret_cast<int32_t *>(ws + L.o_parts);
+  a.partial = reinterpret_cast<float *>(ws + L.o_partial);
+  hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {
+    return kd::launch_valid_count(mask, (int)T, tau, nullptr, scal, s);
+  });
+  if (e != hipSuccess) return hip_fail(e);
+  e = logged(KD_KERNEL_DIVERGENCE, s, [&] { return kd::launch_div(a, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = logged(KD_KERNEL_FINAL_LOSS, s, [&] {
+    return kd::launch_final_loss(rl, (int)T, scal, loss, s);
+  });
+  return e == hipSuccess ? KD_OK : hip_fail(e);
+}
+
 int kd_entropy_filter_workspace_size(int64_t T, size_t *bytes_out) {
   if (!bytes_out || T < 1) return KD_ERR_INVALID_ARG;
   if (T >= (int64_t(1) << 31)) return KD_ERR_UNSUPPORTED;

@@ -178,6 +178,38 @@ struct FilterArgs {
 };
 hipError_t launch_entropy_filter(const FilterArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Reverse KL / Jensen-Shannon divergence over the cached top-K support.
+constexpr int DIV_UNIT = 1024;     // pairs per unit of the dW reduction
+constexpr int RADIX_BLOCK = 4096;  // keys per block of the radix sort
+struct DivArgs {
+  const void *H;            // [T, d] element type
+  const void *W;            // [V, d] element type
+  const int32_t *topk_idx;  // [T, K]
+  const float *topk_logit;  // [T, K]
+  const uint8_t *mask;      // [T] or null
+  const Scalars *scal;
+  int64_t T;
+  int d, V, K;
+  float inv_tau;
+  int kind;                 // KD_DIV_REVERSE_KL or KD_DIV_JSD
+  int bf16;                 // element type of H and W
+  int accumulate;           // dW += instead of dW =
+  float *Gk;                // [T, K] logit gradient at the ids
+  float *row_loss;          // [T] mask * D_t
+  float *dH;                // [T, d]
+  float *dW;                // [V, d]
+  int32_t *keys[2];         // [T K] radix sort keys (ping-pong)
+  int32_t *vals[2];         // [T K] pair indices (ping-pong)
+  int32_t *hist;            // [256 * blocks] digit counts, then offsets
+  int32_t *seg;             // [V + 1] first sorted pair of each id
+  int32_t *unit_start;      // [V + 1] units per id, then their first index
+  int32_t *part_start;      // [V + 1] partial rows per id, then first row
+  float *partial;           // [2 ceil(T K / DIV_UNIT), d] partial dW rows
+};
+int radix_passes(int64_t V);
+hipError_t launch_div(const DivArgs &a, hipStream_t s);
+
 hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s);
 hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s);
 hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s);
