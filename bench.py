@@ -223,6 +223,10 @@ def main():
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", default="1024,2048,4096,8192",
+                    help="slice sizes timed after the main measurement (loss "
+                         "op; a few steps each, reported as chunk_sweep); "
+                         "empty to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc "
@@ -442,9 +446,56 @@ def main():
         "kernel_ms_one_step": split,
         "roofline": roof,
     }
+    if args.op == "loss" and args.sweep:
+        out["chunk_sweep"] = chunk_sweep(
+            lib, (H, W, idx, lg, mptr, dt_code), x, ws, stream,
+            [int(c) for c in args.sweep.split(",")])
     if not args.no_cpu_baseline and args.op == "loss":
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def chunk_sweep(lib, inputs, x, ws, stream, chunks, steps=3):
+    """kd_topk_kl_fwd_bwd at other slice sizes on the same inputs: per slice
+    size, one warm-up call and `steps` timed calls (HIP events on the call's
+    stream), the workspace it needs and the loss (equal for every size)."""
+    import torch
+    import top_kl_loss_amd as kd
+    from top_kl_loss_amd import hip
+    H, W, idx, lg, mptr, dt_code = inputs
+    T, d, V, K = x.T, x.d, x.V, x.K
+    f32 = dict(dtype=torch.float32, device=H.device)
+    loss, dH, dW = torch.empty(1, **f32), torch.empty(T, d, **f32), torch.empty(V, d, **f32)
+    res = []
+    for c in chunks:
+        need = kd.kd_topk_kl_workspace_size(T, d, V, K, c, dt_code)
+        buf = ws if need <= ws.numel() else torch.empty(need, dtype=torch.uint8,
+                                                        device=H.device)
+
+        def call():
+            st = lib.kd_topk_kl_fwd_bwd(
+                H.data_ptr(), W.data_ptr(), dt_code, idx.data_ptr(), lg.data_ptr(),
+                mptr, T, d, V, K, float(x.tau), c, 0, loss.data_ptr(), None,
+                dH.data_ptr(), dW.data_ptr(), buf.data_ptr(), need, stream.value)
+            if st != 0:
+                raise RuntimeError(kd.kd_status_string(st))
+
+        call()
+        ev = [hip.Event() for _ in range(steps + 1)]
+        for i in range(steps):
+            ev[i].record(stream.value)
+            call()
+        ev[steps].record(stream.value)
+        stream.synchronize()
+        ms = sorted(ev[i].elapsed_ms(ev[i + 1]) for i in range(steps))
+        med = ms[len(ms) // 2]
+        res.append({"chunk": c, "ms_per_step": round(med, 3),
+                    "tokens_per_s": round(T / (med * 1e-3), 1),
+                    "tflops": round(6.0 * T * d * V / (med * 1e-3) / 1e12, 2),
+                    "workspace_bytes": need, "loss": float(loss.item())})
+        log(f"chunk {c}: {med:.2f} ms per step, workspace {need / 1e9:.2f} GB")
+        del buf
+    return res
 
 
 TEACHER_METRIC = ("tokens/s & TFLOP/s teacher top-100 cache build (LM-head GEMM + "
