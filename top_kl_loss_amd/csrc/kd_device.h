@@ -65,6 +65,17 @@ template <> struct Elem<float> {
   }
 };
 
+// Linear workgroup id -> id in an order where consecutive ids run on the
+// same XCD (the hardware deals workgroups round-robin over the 8 XCDs of the
+// chip), so tiles that share an operand share an L2.
+__device__ __forceinline__ int xcd_swizzle(int bid, int n) {
+  constexpr int NX = 8;
+  const int per = (n + NX - 1) / NX;
+  const int tall = n % NX == 0 ? NX : n % NX;
+  const int x = bid % NX, local = bid / NX;
+  return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
+}
+
 // Wave-wide (64-lane) reductions through cross-lane shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -1,7 +1,8 @@
 // The three matrix-core GEMMs of the fused, chunked top-K KL loss on gfx950.
 //
 //  logits:  Z = H_c W^T        (C x V, K = d)   with a softmax-statistics and
-//           teacher-gather epilogue; stores P = exp(z/tau - shift_seg)
+//           teacher-gather epilogue; stores P = 2^(z s2 - shift_seg) (base-2
+//           units, s2 = log2(e) / tau)
 //  dH:      dH_c = G W         (C x d, K = V)   split-K over vocabulary
 //  dW:      dW (+)= G^T H_c    (V x d, K = C)
 //
@@ -43,17 +44,6 @@ struct Tile {
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * ROWB + ((chunk ^ (row & 7)) << 4);
-}
-
-// Linear workgroup id -> id in an order where consecutive ids run on the
-// same XCD (the hardware deals workgroups round-robin over the 8 XCDs), so
-// tiles that share an operand share an L2.
-__device__ __forceinline__ int xcd_swizzle(int bid, int n) {
-  constexpr int NX = 8;
-  const int per = (n + NX - 1) / NX;
-  const int tall = n % NX == 0 ? NX : n % NX;
-  const int x = bid % NX, local = bid / NX;
-  return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
 }
 
 // ---------------------------------------------------------------- loaders

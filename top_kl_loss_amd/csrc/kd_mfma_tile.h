@@ -210,14 +210,6 @@ __device__ __forceinline__ void kstep(const char *ta, const char *tb, int ar, in
   }
 }
 
-__device__ __forceinline__ int xcd_swizzle(int bid, int n) {
-  constexpr int NX = 8;
-  const int per = (n + NX - 1) / NX;
-  const int tall = n % NX == 0 ? NX : n % NX;
-  const int x = bid % NX, local = bid / NX;
-  return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
-}
-
 // Grouped tile order: tiles run in groups of GM consecutive M-tiles, the
 // M index fastest, then N, so the ~32 tiles an XCD runs at once form a
 // GM x (32/GM) block whose operand slices are shared through its L2.
@@ -245,9 +237,14 @@ __device__ __forceinline__ void group_tile(int L, int nm, int nn, int gm_max, in
 //
 // The MFMAs are inline asm with the accumulator tied ("+a"), which keeps the
 // compiler from copying accumulators between AGPRs and keeps the source
-// order.  The compiler's hazard checks do not see asm: the first MFMA of
-// every accumulator takes srcC = 0 (no VALU zeroing), and acc_ready() pads
-// with s_nop before the accumulators are read.  LDS layout as above, with
+// order.  The compiler's hazard checks do not see asm, so two rules stand
+// in for them: the first MFMA of every accumulator takes the inline constant
+// 0 as srcC, so no VALU write (zeroing) ever precedes an MFMA read of the
+// same register (the VALU-write -> MFMA-srcC dependency of the ISA's
+// data-dependency table cannot arise; later MFMAs on an accumulator follow
+// MFMAs of the same shape, which the hardware orders itself), and
+// acc_ready() pads with s_nop before the accumulators are read by VALU
+// instructions.  LDS layout as above, with
 // swz4(row) = (row & 7) ^ ((row >> 3) & 1), which is the same for rows 16
 // apart, so a fragment address is one register plus an immediate.
 namespace w4 {
@@ -428,7 +425,10 @@ __device__ __forceinline__ void nt_loop(Copy<S::RA> &ca, Copy<S::RB> &cb, int kb
 }
 
 // Wait states between the last MFMA and the first read of its accumulator
-// (the hazard check does not see the asm MFMAs); the empty asm statements
+// (the compiler's hazard check does not see the asm MFMAs): 4 x s_nop 7 =
+// 32, more than the largest XDL-write -> VALU-read requirement of the
+// CDNA3/CDNA4 data-dependency table (18-19 wait states, for 16-pass MFMAs;
+// the 16x16x32 MFMAs here take fewer passes).  The empty asm statements
 // order every accumulator read after the padding.
 template <int TMB, int TNB>
 __device__ __forceinline__ void acc_ready(f32x4 (&acc)[TMB][TNB]) {
