@@ -47,7 +47,6 @@ TRAFFIC_KERNELS = {
              ("k_fast_dh", "gemm_dh", _GEMM_SRC),
              ("k_fast_dw", "gemm_dw", _GEMM_SRC),
              ("k_fast_logits_redo(", "flagged_rows", _GEMM_SRC),
-             ("k_transpose_w(", "transpose_w", _GEMM_SRC),
              ("k_transpose_h(", "transpose_h", _GEMM_SRC),
              ("k_lse_fix<", "lse_fix", _ROW_SRC),
              ("k_reduce_dh(", "reduce_dh", _ROW_SRC),

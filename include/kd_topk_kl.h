@@ -86,10 +86,8 @@ enum {
  * element type), per-row and per-vocabulary-segment softmax statistics,
  * the teacher distribution of the slice, split-K partial sums of dH for the
  * slice and O(T) per-row scalars; on the tuned bf16 path also the
- * transposed gradient (V x chunk) and hidden states (d x chunk) of the
- * slice and, when chunk >= d, one transposed copy of W (d x V bf16, no
- * larger than the slice's gradient).  It grows with chunk*V and chunk*d,
- * never with T*V.
+ * transposed, gradient-scaled hidden states of the slice (d x chunk).  It
+ * grows with chunk*V and chunk*d, never with T*V.
  *
  * Arguments: sizes as for kd_topk_kl_fwd_bwd; `chunk` is clamped to [1, T].
  * `bytes_out` (host pointer) receives the size.  Returns KD_OK,
@@ -273,7 +271,7 @@ enum {
   KD_KERNEL_TRANSPOSE_H = 8, /* H_c^T staging for the dW GEMM (bf16 path)    */
   KD_KERNEL_FLAGGED_ROWS = 9, /* bf16 path: rows whose a-priori shift was too
                                 low, recomputed with the row maximum         */
-  KD_KERNEL_TRANSPOSE_W = 10, /* W^T once per call (bf16 path, chunk >= d)   */
+  /* id 10 is not used */
   /* kd_teacher_topk */
   KD_KERNEL_TK_SAMPLE = 11,  /* logits of the sampled vocabulary segments    */
   KD_KERNEL_TK_THETA = 12,   /* per-row threshold from the sampled logits    */

@@ -38,7 +38,7 @@ def _case(name, case, T, d, V, dtype, tau, noise, chunk, mask_frac=0.1, K=100):
 
 
 CASES = [
-    # tuned bf16 kernels (d % 64 == 0): with and without the W^T copy.  The
+    # tuned bf16 kernels (d % 64 == 0): slices below and above d.  The
     # noise sets |p - q| / p at the ids to about 5% (noise / tau = 0.05): a
     # gradient formed from p rounded to bf16 (relative error 2^-9) and then
     # reduced by q would miss the 2e-2 bar there.

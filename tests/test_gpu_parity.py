@@ -151,18 +151,18 @@ def test_bf16_tuned_path_reshift_and_small_slices():
     check_case(x)
 
 
-def test_bf16_tuned_path_with_transposed_weight_copy():
-    # chunk >= d: the dH GEMM reads a W^T copy made once per call; V and T
-    # ragged, padding rows
+def test_bf16_tuned_path_chunk_above_d():
+    # chunk >= d; V and T ragged, padding rows
     x = synth.make_case("bf16_wt", case=32, T=600, d=192, V=3001, K=50,
                         dtype="bf16", tau=1.1, mask_frac=0.05, chunk=256)
     check_case(x)
 
 
-def test_bf16_tuned_path_wide_tiles_with_transposed_weight_copy():
-    # d a multiple of 320: dW runs on 192 x 320 tiles, dH on 256 x 256 tiles
-    # with a ragged N tile (W^T copy since chunk >= d); ragged T, V (192-row
-    # tiles), padding rows
+def test_bf16_tuned_path_wide_tiles():
+    # d a multiple of 320: dW runs on 192 x 320 tiles (its P~ operand read
+    # with 24-chunk k-rows), dH on 256 x 256 tiles with a ragged N tile whose
+    # W columns past d come from the next W row; ragged T, V (192-row tiles),
+    # padding rows
     x = synth.make_case("bf16_wide", case=33, T=900, d=640, V=3001, K=64,
                         dtype="bf16", tau=1.2, mask_frac=0.05, chunk=640)
     check_case(x)

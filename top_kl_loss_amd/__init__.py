@@ -53,7 +53,7 @@ KD_FILTER_ENTROPY_ABOVE, KD_FILTER_TOP_ENTROPY_FRACTION = 0, 1
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
                 "gemm_dh", "reduce_dh", "gemm_dw", "final_loss", "transpose_h",
-                "flagged_rows", "transpose_w", "tk_sample", "tk_theta", "tk_filter",
+                "flagged_rows", "unused_10", "tk_sample", "tk_theta", "tk_filter",
                 "tk_select", "tk_stream", "grad_cast", "entropy_filter",
                 "divergence")
 

@@ -52,9 +52,8 @@ struct Layout {
   bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_lq, o_zg, o_sid, o_sslot, o_first,
-      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_gt, o_wt, o_shift,
-      o_frow, o_flag, o_tflag;
-  bool wt;
+      o_mseg, o_sseg, o_fseg, o_lse, o_P, o_dhp, o_ht, o_shift, o_frow, o_flag,
+      o_tflag;
   int dh_bn, dw_bn;
   int ldh;
   size_t total;
@@ -75,8 +74,8 @@ int check_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
 }
 
 // fwd_only: the regions the forward alone touches (no probabilities, G,
-// gradient factors, dH partials or transposed copies): the compact layout of
-// the allocation-free forward entry point.
+// gradient factors, dH partials or the transposed hidden states): the
+// compact layout of the allocation-free forward entry point.
 Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
                    kd_dtype dtype, bool fwd_only = false) {
   Layout L{};
@@ -84,10 +83,6 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
   L.ldp = L.nseg * kd::SEG;
   L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, L.ldp);
-  // A W^T copy (V x d bf16) lets the dH GEMM copy both operands by DMA; it is
-  // kept only when it is no larger than one slice's G (C >= d), so the extra
-  // memory stays bounded by a slice.
-  L.wt = L.fast && (int64_t)L.C >= d;
   L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;  // dW: 192 x 320 tiles when 320
   L.dh_bn = 256;                                   // dH: 256 x 256 tiles
   L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast, L.dh_bn);
@@ -112,8 +107,6 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.o_dhp = take(g * sizeof(float) * (size_t)L.splits * C * (size_t)d);
   L.ldh = (int)((C + 63) / 64 * 64);
   L.o_ht = take(g * (L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0));
-  L.o_gt = take(g * (L.fast ? sizeof(uint16_t) * (size_t)L.ldp * L.ldh : 0));
-  L.o_wt = take(g * (L.wt ? sizeof(uint16_t) * (size_t)d * L.ldp : 0));
   L.o_shift = take(g * sizeof(float) * C);
   L.o_frow = take(g * sizeof(float) * C);
   L.o_flag = take(g * sizeof(int32_t) * C);
@@ -247,12 +240,10 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
   a.P = ws + L.o_P;
   a.dh_part = reinterpret_cast<float *>(ws + L.o_dhp);
   a.Ht = reinterpret_cast<uint16_t *>(ws + L.o_ht);
-  a.Gt = reinterpret_cast<uint16_t *>(ws + L.o_gt);
   a.shift = reinterpret_cast<float *>(ws + L.o_shift);
   a.frow = reinterpret_cast<float *>(ws + L.o_frow);
   a.flag = reinterpret_cast<int32_t *>(ws + L.o_flag);
   a.tile_flags = reinterpret_cast<int32_t *>(ws + L.o_tflag);
-  a.Wt = (L.wt && grads) ? reinterpret_cast<uint16_t *>(ws + L.o_wt) : nullptr;
   a.ldh = L.ldh;
   a.dh_stride = (size_t)L.C * (size_t)d;
   a.splits = L.splits;
@@ -270,10 +261,6 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
                                   scal, s);
   });
   if (e != hipSuccess) return hip_fail(e);
-  if (a.Wt) {
-    e = logged(KD_KERNEL_TRANSPOSE_W, s, [&] { return kd::launch_transpose_w(a, s); });
-    if (e != hipSuccess) return hip_fail(e);
-  }
   for (int64_t c0 = 0; c0 < T; c0 += L.C) {
     a.c0 = c0;
     a.C = (int)(T - c0 < L.C ? T - c0 : L.C);

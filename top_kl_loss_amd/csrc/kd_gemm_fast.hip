@@ -4,13 +4,15 @@
 //
 //  logits:  Z = H_c W^T      (C x V, K = d)   + softmax-statistics epilogue
 //  dH:      dH_c = G W       (C x d, K = V)   split-K over the vocabulary
-//  dW:      dW (+)= G^T H_c  (V x d, K = C)   operands P~^T and (f H_c)^T
+//  dW:      dW (+)= G^T H_c  (V x d, K = C)   operands P~ and (f H_c)^T
 // The logits GEMM stores the slice's probabilities P~ = 2^(z s2 - sh_t) with
-// one a-priori shift per row, in bf16, row-major and transposed; k_lse_fix
-// applies the teacher correction at the ids and the per-row gradient factor
-// f_t, so that G = f_t P~.  dH = f_t (P~ W) (the factor applied when the
-// split-K partials are reduced) and dW = P~^T (f H_c) (k_transpose_h writes
-// (f H_c)^T).
+// one a-priori shift per row, in bf16, row-major; k_lse_fix applies the
+// teacher correction at the ids and defines the per-row gradient factor f_t,
+// so that G = f_t P~.  dH = f_t (P~ W) (the factor applied when the split-K
+// partials are reduced) and dW = P~^T (f H_c) (k_transpose_h writes
+// (f H_c)^T).  The dH GEMM reads W and the dW GEMM reads P~ as stored, their
+// mn index contiguous (transposing LDS reads), so neither needs a
+// transposed copy.
 //
 // The tile machinery (4-wave and 8-wave tiles, DMA operand copies, swizzled
 // LDS layouts, MFMA schedules) is in kd_mfma_tile.h.
@@ -34,10 +36,7 @@ using namespace tile;
 //    2^(z s2 - shift) (the softmax statistics), z itself at the row's teacher
 //    ids inside the segment (the student-logit gather), and, when gradients
 //    are wanted, the probabilities with the row's a-priori shift sh_t,
-//    P~ = 2^(z s2 - sh_t), stored in bf16 twice: row-major [C, ldp] (the dH
-//    operand) and transposed [ldp, ldh] (the dW operand, tokens contiguous),
-//    the latter from a transposed copy in LDS so that every store writes
-//    whole 128-byte lines.  Rows at or past C are stored as 0 in P~^T.
+//    P~ = 2^(z s2 - sh_t), stored in bf16, row-major [C, ldp].
 //  MODE 1: the same logits, stored only for the rows flagged by k_lse_fix,
 //    with their exact maximum as shift (no statistics, no gather).
 // The wave tiles interleave their 16-row blocks (w4::SquareI: block i of
@@ -46,10 +45,7 @@ using namespace tile;
 // blocks 2p and 2p + 1 of both wave rows, and stage row sr is tile row
 // 64 p + sr.  Thread (pr, part) = (tid / 8, tid % 8) takes the two rows
 // 2 pr and 2 pr + 1 and the 8-column groups part, part + 8, ... of them, so
-// the 8 threads of a row store whole lines of P~ and each thread packs the
-// pair of adjacent tokens of a column into one word of the transposed copy
-// (word (col, pr) at col * 32 + 4 ((pr >> 2) ^ ((col >> 3) & 7)) + (pr & 3):
-// 16-byte chunks XOR-swizzled per column).
+// the 8 threads of a row store whole 128-byte lines of P~.
 template <int MODE>
 __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg, char *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -112,7 +108,6 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
   constexpr int PITCH = BN + 4;
   constexpr int TPR = 8, CPT = BN / TPR;
   float *stage = reinterpret_cast<float *>(lds);
-  uint32_t *tb = reinterpret_cast<uint32_t *>(lds + 64 * PITCH * 4);
   uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
   const float s2 = a.s2;
   const bool tail = n0 + BN > a.V;
@@ -129,9 +124,8 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
     __syncthreads();
     // Rows one at a time (fewer live registers): z of the row (-inf past V:
     // only the vocabulary's last segment has such columns), the statistics,
-    // and P~ packed to bf16 pairs of adjacent columns, pk[q][c / 2].
+    // and P~ packed to bf16 pairs of adjacent columns.
     const int r0 = m0 + 64 * pass + 2 * pr;
-    uint32_t pk[2][CPT / 2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float v[CPT];
@@ -174,40 +168,16 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
 #pragma unroll
         for (int c = 0; c < CPT; ++c) v[c] = __builtin_amdgcn_exp2f(fmaf(v[c], s2, -sh[pass][q]));
       }
-      if (grads) {
+      // rows past C (and, in MODE 1, rows not flagged: +inf shift) are not
+      // stored
+      const int r = r0 + q;
+      if (grads && r < a.C && (MODE == 0 || sh[pass][q] != INFINITY)) {
+        uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
 #pragma unroll
-        for (int c = 0; c < CPT; c += 2) pk[q][c / 2] = pack_bf16x2(v[c], v[c + 1]);
-        // rows past C (and, in MODE 1, rows not flagged) hold +inf shifts:
-        // their P~ is 0, stored only into the transposed copy in MODE 0
-        const int r = r0 + q;
-        if (r < a.C && (MODE == 0 || sh[pass][q] != INFINITY)) {
-          uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
-#pragma unroll
-          for (int j = 0; j < CPT / 8; ++j)
-            *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) =
-                u32x4{pk[q][4 * j], pk[q][4 * j + 1], pk[q][4 * j + 2], pk[q][4 * j + 3]};
-          if (MODE == 1) {
-            // flagged rows are rare: their transposed entries one by one
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-              const int col = (c >> 3) * 8 * TPR + part * 8 + (c & 7);
-              a.Gt[(size_t)(n0 + col) * a.ldh + r] =
-                  uint16_t((c & 1) ? pk[q][c / 2] >> 16 : pk[q][c / 2] & 0xffffu);
-            }
-          }
-        }
-      }
-    }
-    if (MODE == 0 && grads) {
-      // the token pair (2 pr, 2 pr + 1) of each column: one word of the
-      // transposed copy; (col >> 3) & 7 == part for all of this thread's
-      // columns, so the chunk is (pr >> 2) ^ part
-      uint32_t *tw = tb + part * 8 * 32 + ((((pr >> 2) ^ part) << 2) + (pr & 3));
-#pragma unroll
-      for (int c = 0; c < CPT; c += 2) {
-        const int col0 = (c >> 3) * 8 * TPR + (c & 7);  // minus part * 8
-        tw[col0 * 32] = __builtin_amdgcn_perm(pk[1][c / 2], pk[0][c / 2], 0x05040100u);
-        tw[(col0 + 1) * 32] = __builtin_amdgcn_perm(pk[1][c / 2], pk[0][c / 2], 0x07060302u);
+        for (int j = 0; j < CPT / 8; ++j)
+          *reinterpret_cast<u32x4 *>(dst + j * 8 * TPR) =
+              u32x4{pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
+                    pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7])};
       }
     }
     // Gather z at the teacher ids: thread tid owns tile row tid, staged in
@@ -236,17 +206,6 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
       }
     }
     __syncthreads();
-    // P~^T rows n0 .. n0 + 255, tokens m0 + 64 pass .. + 63: 16 bytes (8
-    // tokens) per thread and column, 8 threads per 128-byte line
-    if (MODE == 0 && grads && m0 + 64 * pass < a.ldh) {
-      const int g = tid & 7;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int col = (tid >> 3) + 32 * i;
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(tb + col * 32 + ((g ^ ((col >> 3) & 7)) << 2));
-        *reinterpret_cast<u32x4 *>(a.Gt + (size_t)(n0 + col) * a.ldh + m0 + 64 * pass + 8 * g) = w;
-      }
-    }
   }
 }
 
@@ -275,68 +234,13 @@ void k_fast_logits_redo(SliceArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- dH GEMM
-// A = G (K-contiguous over the vocabulary; copied by DMA), B = W
-// (vocabulary rows, hidden contiguous) transposed through registers: the
-// 8-wave path for calls without a W^T copy (slices smaller than d).  With
-// the copy, k_fast_dh4 below runs instead.
-__global__ __launch_bounds__(NT, 1) void k_fast_dh_reg(SliceArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int nmt = (a.C + BM - 1) / BM;
-  const int nnt = (a.d + BN - 1) / BN;
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int split = tile / (nnt * nmt);
-  int mt, nt;
-  group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
-  const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
-  const int kbeg = sbeg * SEG, kend = send * SEG;
-  CopyK<8> ca;
-  ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-  f32x16 acc[TM][TN];
-  zero_acc(acc);
-  const int nk = (kend - kbeg) / BK;
-  const int ar = wm * WTM + (lane & 31), br = wn * WTN + (lane & 31), hh = lane >> 5;
-  RegMN4 rb;
-  rb.init(reinterpret_cast<const uint16_t *>(a.W), a.d, n0, a.d, kend < a.V ? kend : a.V, tid);
-  ca.issue(lds, kbeg);
-  rb.load(kbeg);
-  rb.store(lds + OP_BYTES, tid);
-  for (int ks = 0; ks < nk; ++ks) {
-    const char *cur = lds + (ks & 1) * STAGE_BYTES;
-    char *nxt = lds + ((ks + 1) & 1) * STAGE_BYTES;
-    const int kn = kbeg + (ks + 1 < nk ? ks + 1 : ks) * BK;
-    wait_vm0();
-    __syncthreads();
-    ca.issue(nxt, kn);
-    rb.load(kn);
-    kstep(cur, cur + OP_BYTES, ar, br, hh, acc);
-    rb.store(nxt + OP_BYTES, tid);
-  }
-  wait_vm0();
-
-  float *out = a.dh_part + (size_t)split * a.dh_stride;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + i * 32 + acc_row(e, lane);
-        if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
-      }
-    }
-}
-
 // ---------------------------------------------------------- dH and dW GEMMs
 // On 4-wave tiles, both operands copied by DMA:
-//  dH partials = G (W^T)^T per vocabulary split, A = G, B = W^T (the call's
-//  W^T copy), 256 x 256 tiles;
-//  dW (+)= G^T (H_c^T)^T, A = G^T, B = H_c^T, 192 x 320 tiles when d is a
+//  dH partials = P~ W per vocabulary split (f applied by the reduction),
+//  A = P~ (K-contiguous), B = W (MN-contiguous: vocabulary rows, hidden
+//  contiguous), 256 x 256 tiles;
+//  dW (+)= P~^T (f H_c), A = P~ (MN-contiguous: token rows, vocabulary
+//  contiguous), B = (f H_c)^T (K-contiguous), 192 x 320 tiles when d is a
 //  multiple of 320 (no N padding; d = 2880 = 9 x 320), else 256 x 256.
 __global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fast_dh4(SliceArgs a) {
@@ -352,11 +256,11 @@ void k_fast_dh4(SliceArgs a) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
-  using S = w4::Square;
+  using S = w4::SquareBMN;
   w4::Copy<S::RA> ca;
-  w4::Copy<S::RB> cb;
+  w4::CopyMN<S::RB> cb;
   ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
-  cb.init(a.Wt, (uint64_t)a.d * a.ldp * 2, a.ldp, n0, wave, lane);
+  cb.init(a.W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
   f32x4 acc[8][8];
   w4::nt_loop<S>(ca, cb, sbeg * SEG, (send - sbeg) * (SEG / BK), lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
@@ -386,9 +290,9 @@ void k_fast_dw4(SliceArgs a) {
   int mt, nt;
   group_tile(tile, nmt, nnt, 4, mt, nt);
   const int m0 = mt * S::RA, n0 = nt * S::RB;
-  w4::Copy<S::RA> ca;
+  w4::CopyMN<S::RA> ca;
   w4::Copy<S::RB> cb;
-  ca.init(a.Gt, (uint64_t)a.ldp * a.ldh * 2, a.ldh, m0, wave, lane);
+  ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
   cb.init(a.Ht, (uint64_t)a.d * a.ldh * 2, a.ldh, n0, wave, lane);
   f32x4 acc[S::TMB][S::TNB];
   w4::nt_loop<S>(ca, cb, 0, (a.C + BK - 1) / BK, lds, wm, wn, lane, acc);
@@ -460,14 +364,8 @@ __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
               a.frow);
 }
 
-// W^T [d, ldp] once per call (vocabulary columns v >= V zero).
-__global__ __launch_bounds__(256) void k_transpose_w(SliceArgs a) {
-  transpose64(reinterpret_cast<const uint16_t *>(a.W), a.d, a.V, a.Wt, a.ldp);
-}
-
 template <typename K>
-hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds = LDS_BYTES,
-                  int threads = NT) {
+hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds, int threads) {
   if (grid <= 0) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -512,21 +410,13 @@ hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
 
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
   const int tiles = ((a.C + BM - 1) / BM) * ((a.d + BN - 1) / BN) * a.splits;
-  if (a.Wt) return launch(k_fast_dh4, tiles, a, s, w4::Square::LDS, w4::NT);
-  return launch(k_fast_dh_reg, tiles, a, s);
+  return launch(k_fast_dh4, tiles, a, s, w4::SquareBMN::LDS, w4::NT);
 }
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
   const dim3 tg(a.ldh / 64, a.d / 64);
   hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s) {
-  if (!a.Wt) return hipSuccess;
-  const dim3 g(a.ldp / 64, a.d / 64);
-  hipLaunchKernelGGL(k_transpose_w, g, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -538,12 +428,12 @@ hipError_t launch_flagged_rows(const SliceArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
-  if (a.dw_bn == w4::Tall::RB) {
-    using S = w4::Tall;
+  if (a.dw_bn == w4::TallAMN::RB) {
+    using S = w4::TallAMN;
     return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
                   S::LDS, w4::NT);
   }
-  using S = w4::Square;
+  using S = w4::SquareAMN;
   return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
                 S::LDS, w4::NT);
 }

@@ -64,12 +64,10 @@ struct SliceArgs {
   float *sseg;       // [Cmax, nseg] segment sum of 2^(z s2 - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
   uint16_t *Ht;      // [d, ldh] bf16 (f H_c)^T (tuned path only)
-  uint16_t *Gt;      // [ldp, ldh] bf16 transposed probabilities P^T (tuned)
   float *shift;      // [Cmax] tuned path: row shift (base-2 units)
   float *frow;       // [Cmax] tuned path: gradient factor f_t of the row
   int32_t *flag;     // [Cmax] tuned path: 1 = row recomputed with its max
   int32_t *tile_flags;  // [ceil(Cmax/ROW_TILE)] flagged rows per M-tile
-  uint16_t *Wt;      // [d, ldp] bf16 W^T (tuned path with C >= d), or null
   int ldh;           // row pitch of Ht: Cmax rounded up to 64
   float *lse;        // [Cmax] row logsumexp of z/tau
   void *P;           // [Cmax, ldp] shifted probabilities, then (after
@@ -106,8 +104,6 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s);
 hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s);
 // H_c^T for the tuned dW GEMM (no-op on the generic path).
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s);
-// Tuned path with a W^T buffer: W^T once per call (before the slices).
-hipError_t launch_transpose_w(const SliceArgs &a, hipStream_t s);
 // Tuned path: rows flagged by k_lse_fix (shift too far below the row
 // maximum) get their probabilities recomputed with the maximum and their
 // teacher correction; no work beyond a flag check when none is flagged.

@@ -176,9 +176,9 @@ __device__ __forceinline__ void row_stats(const SliceArgs &a, int r, int lane, f
   log2s = log2f(wave_sum(s));
 }
 
-// Tuned path: the teacher correction of row r with the row's shift sh, in
-// both stored layouts: at every valid teacher id,
-//   P~[r, id] = P~^T[id, r] = 2^(z_k s2 - sh) - q_k 2^(M + log2 s - sh),
+// Tuned path: the teacher correction of row r with the row's shift sh: at
+// every valid teacher id,
+//   P~[r, id] = 2^(z_k s2 - sh) - q_k 2^(M + log2 s - sh),
 // from the fp32 logit z_k, rounded once to bf16.
 __device__ __forceinline__ void correct_rows_tuned(const SliceArgs &a, int r, int lane, float sh,
                                                    float mx, float log2s) {
@@ -192,9 +192,7 @@ __device__ __forceinline__ void correct_rows_tuned(const SliceArgs &a, int r, in
     const int id = a.topk_idx[t * K + k];
     if (id < 0 || id >= a.V) continue;
     const float val = exp2f(fmaf(zg[k], a.s2, -sh)) - q[k] * corr;
-    const uint16_t b = uint16_t(f32_to_bf16_rne(val));
-    P[id] = b;
-    a.Gt[(size_t)id * a.ldh + r] = b;
+    P[id] = uint16_t(f32_to_bf16_rne(val));
   }
 }
 
@@ -324,7 +322,7 @@ __global__ __launch_bounds__(256) void k_lse_fix(SliceArgs a) {
 }
 
 // Tuned path, after k_fast_logits_redo: the teacher correction of the
-// flagged rows (shift = row maximum), in both stored layouts.
+// flagged rows (shift = row maximum).
 __global__ __launch_bounds__(256) void k_fix_flagged(SliceArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * ROWS_PER_WG + wave;
