@@ -46,8 +46,14 @@ def test_workspace_size_scales_with_chunk_not_with_T():
     dense = 8 * 32768 * 201088          # fp32 logits + fp32 gradient
     assert a < dense / 50
     assert a - b < 32768 * 4 * 2        # only O(T) scalars grow with T
-    c = kd.kd_topk_kl_workspace_size(32768, 2880, 201088, 100, 2048, kd.KD_BF16)
-    assert 1.5 * a < c < 2.2 * a
+    ws = [kd.kd_topk_kl_workspace_size(32768, 2880, 201088, 100, c, kd.KD_BF16)
+          for c in (2048, 4096, 8192)]
+    # from 2048 tokens on, one slice's probabilities are resident
+    assert 1.8 * ws[0] < ws[1] < 2.2 * ws[0] and 1.8 * ws[1] < ws[2] < 2.2 * ws[1]
+    # below, the tuned path keeps those of up to 4 slices (until 2048
+    # tokens) for one dW GEMM per group: chunk 1024 holds two, about what
+    # chunk 2048 holds, and stays near 1 GB at this shape
+    assert 0.9 * ws[0] < a < 1.1 * ws[0] and a < 1.1e9
     # chunk is clamped to T
     assert (kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 64, kd.KD_F32) <
             kd.kd_topk_kl_workspace_size(256, 512, 8192, 100, 10 ** 6, kd.KD_F32)

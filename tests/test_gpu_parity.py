@@ -128,8 +128,8 @@ def test_repeat_is_bitwise_identical_and_accumulate_adds():
 def test_bf16_tuned_path_ragged_tails():
     # d a multiple of 64 (tuned kernels) but not of the 256-wide tiles, V not
     # a multiple of the segment, chunk not a multiple of the 256-row tile nor
-    # of the 64-token k-step of dW, chunk < d (dH transposes W through
-    # registers), T not a multiple of chunk, padding rows, tau != 1.
+    # of the 64-token k-step of dW (so one dW GEMM per slice), chunk < d, T
+    # not a multiple of chunk, padding rows, tau != 1.
     x = synth.make_case("bf16_tuned_ragged", case=30, T=700, d=320, V=3001,
                         K=37, dtype="bf16", tau=1.3, mask_frac=0.1, chunk=300)
     check_case(x)
@@ -149,6 +149,18 @@ def test_bf16_tuned_path_reshift_and_small_slices():
     x.H_bits = synth.f32_to_bf16_bits(H)
     x.H = synth.bf16_bits_to_f32(x.H_bits)
     check_case(x)
+
+
+def test_bf16_tuned_path_dw_groups():
+    # chunk a multiple of 64 below 2048 tokens: the probabilities of several
+    # slices stay resident and dW runs once per group (4 slices of 128, then
+    # 2 of 1024), the last group ending in a ragged slice
+    x = synth.make_case("bf16_groups", case=40, T=1000, d=192, V=3001, K=40,
+                        dtype="bf16", tau=0.9, mask_frac=0.05, chunk=128)
+    check_case(x)
+    y = synth.make_case("bf16_groups2", case=41, T=2100, d=64, V=2000, K=30,
+                        dtype="bf16", tau=1.0, mask_frac=0.05, chunk=1024)
+    check_case(y)
 
 
 def test_bf16_tuned_path_chunk_above_d():

@@ -49,6 +49,7 @@ hipError_t logged(int kind, hipStream_t s, F &&launch) {
 
 struct Layout {
   int C, nseg, ldp, splits;
+  int G;  // slices per dW group (tuned path)
   bool fast;
   size_t esize;
   size_t o_scal, o_rowloss, o_q, o_lq, o_zg, o_sid, o_sslot, o_first,
@@ -83,6 +84,20 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
   L.ldp = L.nseg * kd::SEG;
   L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, L.ldp);
+  // The tuned path keeps the probabilities of G consecutive slices and runs
+  // the dW GEMM once per group, over G C tokens: every dW GEMM reads and
+  // writes all of dW (V x d fp32), so small slices would otherwise spend
+  // more time on that traffic than on the product.  Up to 4 slices, until
+  // 2048 tokens (C a multiple of 64, so that the group's transposed hidden
+  // states stay 16-byte aligned per slice).
+  L.G = 1;
+  if (L.fast && L.C % 64 == 0 && L.C < 2048) {
+    const int64_t nsl = (T + L.C - 1) / L.C;
+    int64_t g = (2048 + L.C - 1) / L.C;
+    if (g > 4) g = 4;
+    if (g > nsl) g = nsl;
+    L.G = (int)g;
+  }
   L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;  // dW: 192 x 320 tiles when 320
   L.dh_bn = 256;                                   // dH: 256 x 256 tiles
   L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast, L.dh_bn);
@@ -103,9 +118,9 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
   const size_t g = fwd_only ? 0 : 1;  // gradient-only regions
   L.o_fseg = take(g * sizeof(float) * C * nseg);
   L.o_lse = take(sizeof(float) * C);
-  L.o_P = take(g * L.esize * C * (size_t)L.ldp);
+  L.o_P = take(g * L.esize * (size_t)L.G * C * (size_t)L.ldp);
   L.o_dhp = take(g * sizeof(float) * (size_t)L.splits * C * (size_t)d);
-  L.ldh = (int)((C + 63) / 64 * 64);
+  L.ldh = (int)(((size_t)L.G * C + 63) / 64 * 64);
   L.o_ht = take(g * (L.fast ? sizeof(uint16_t) * (size_t)d * L.ldh : 0));
   L.o_shift = take(g * sizeof(float) * C);
   L.o_frow = take(g * sizeof(float) * C);
@@ -262,9 +277,11 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
   });
   if (e != hipSuccess) return hip_fail(e);
   for (int64_t c0 = 0; c0 < T; c0 += L.C) {
+    const int j = (int)((c0 / L.C) % L.G);  // slice within its dW group
     a.c0 = c0;
     a.C = (int)(T - c0 < L.C ? T - c0 : L.C);
-    a.dw_beta = (c0 > 0 || (flags & KD_FLAG_ACCUMULATE_DW)) ? 1 : 0;
+    a.P = ws + L.o_P + (size_t)j * L.C * L.ldp * L.esize;
+    a.ht_col = j * L.C;
     if ((e = logged(KD_KERNEL_PREP_ROWS, s, [&] { return kd::launch_prep_rows(a, s); })) ||
         (e = logged(KD_KERNEL_GEMM_LOGITS, s, [&] { return kd::launch_gemm_logits(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_LSE_FIX, s, [&] { return kd::launch_lse_fix(a, bf16, s); })))
@@ -273,9 +290,18 @@ int run_loss(LossMode mode, const void *H, const void *W, kd_dtype dtype,
     if ((a.fast && (e = logged(KD_KERNEL_FLAGGED_ROWS, s, [&] { return kd::launch_flagged_rows(a, s); }))) ||
         (e = logged(KD_KERNEL_GEMM_DH, s, [&] { return kd::launch_gemm_dh(a, bf16, s); })) ||
         (e = logged(KD_KERNEL_REDUCE_DH, s, [&] { return kd::launch_reduce_dh(a, s); })) ||
-        (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))) ||
-        (e = logged(KD_KERNEL_GEMM_DW, s, [&] { return kd::launch_gemm_dw(a, bf16, s); })))
+        (a.fast && (e = logged(KD_KERNEL_TRANSPOSE_H, s, [&] { return kd::launch_transpose_h(a, s); }))))
       return hip_fail(e);
+    if (j == L.G - 1 || c0 + a.C >= T) {
+      // dW over the group: its first slice's rows onwards
+      kd::SliceArgs b = a;
+      b.c0 = c0 - (int64_t)j * L.C;
+      b.C = (int)(c0 + a.C - b.c0);
+      b.P = ws + L.o_P;
+      b.dw_beta = (b.c0 > 0 || (flags & KD_FLAG_ACCUMULATE_DW)) ? 1 : 0;
+      e = logged(KD_KERNEL_GEMM_DW, s, [&] { return kd::launch_gemm_dw(b, bf16, s); });
+      if (e != hipSuccess) return hip_fail(e);
+    }
   }
   if (mode != MODE_BWD) {
     e = logged(KD_KERNEL_FINAL_LOSS, s, [&] {

@@ -319,8 +319,9 @@ void k_fast_dw4(SliceArgs a) {
 }
 
 // dst[j * ldd + r] = src[r * d + j] (times rscale[r] when rscale is not
-// null, rounded to nearest even) for r < nrows, 0 for nrows <= r < ldd
-// (bf16, d and ldd multiples of 64), over 64 (r) x 64 (j) tiles: 16-byte
+// null, rounded to nearest even) for r < nrows, 0 for nrows <= r < 64
+// gridDim.x (bf16, d and ldd multiples of 64, dst 16-byte aligned), over
+// 64 (r) x 64 (j) tiles: 16-byte
 // loads of the source rows, a transposing read from LDS, 16-byte stores of
 // the destination rows.  256 threads.
 __device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, int64_t d, int nrows,
@@ -356,12 +357,12 @@ __device__ __forceinline__ void transpose64(const uint16_t *__restrict__ src, in
   }
 }
 
-// (f H_c)^T [d, ldh] per slice, each token row scaled by its gradient
-// factor f_t (token columns t >= C zero): with P~^T this gives
-// dW = P~^T (f H_c) = G^T H_c.
+// The slice's columns ht_col .. of (f H)^T [d, ldh], each token row scaled
+// by its gradient factor f_t (columns past the slice's C tokens, up to the
+// next multiple of 64, zero): dW = P~^T (f H) = G^T H over the group.
 __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
-  transpose64(reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d, a.d, a.C, a.Ht, a.ldh,
-              a.frow);
+  transpose64(reinterpret_cast<const uint16_t *>(a.H) + a.c0 * a.d, a.d, a.C, a.Ht + a.ht_col,
+              a.ldh, a.frow);
 }
 
 template <typename K>
@@ -415,7 +416,7 @@ hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
-  const dim3 tg(a.ldh / 64, a.d / 64);
+  const dim3 tg((a.C + 63) / 64, a.d / 64);
   hipLaunchKernelGGL(k_transpose_h, tg, dim3(256), 0, s, a);
   return hipGetLastError();
 }

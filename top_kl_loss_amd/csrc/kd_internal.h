@@ -63,15 +63,17 @@ struct SliceArgs {
   float *mseg;       // [Cmax, nseg] segment max of z s2 (shift, base-2 units)
   float *sseg;       // [Cmax, nseg] segment sum of 2^(z s2 - shift)
   float *fseg;       // [Cmax, nseg] tau/N * mask * exp(shift - lse)
-  uint16_t *Ht;      // [d, ldh] bf16 (f H_c)^T (tuned path only)
+  uint16_t *Ht;      // [d, ldh] bf16 (f H)^T of the dW group's tokens (tuned)
+  int ht_col;        // tuned path: column of Ht where this slice's tokens go
   float *shift;      // [Cmax] tuned path: row shift (base-2 units)
   float *frow;       // [Cmax] tuned path: gradient factor f_t of the row
   int32_t *flag;     // [Cmax] tuned path: 1 = row recomputed with its max
   int32_t *tile_flags;  // [ceil(Cmax/ROW_TILE)] flagged rows per M-tile
-  int ldh;           // row pitch of Ht: Cmax rounded up to 64
+  int ldh;           // row pitch of Ht: the dW group's tokens rounded up to 64
   float *lse;        // [Cmax] row logsumexp of z/tau
   void *P;           // [Cmax, ldp] shifted probabilities, then (after
-                     // k_lse_fix) the logit gradient G (element type)
+                     // k_lse_fix) the logit gradient G (element type); for
+                     // the dW GEMM, the group's rows (C of them)
   float *dh_part;    // [splits, Cmax, d] split-K partial sums of dH
   size_t dh_stride;  // elements between two partials (Cmax * d)
   int splits;
