@@ -85,15 +85,19 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
   // over its SHIFT_SLOTS best teacher slots (teacher logit descending, equal
   // logits by slot), from fp32 dot products of the bf16 rows of H and W.
   // Each is an actual logit of the row up to rounding, so the shift lies at
-  // or below the row maximum; -inf when no slot holds a valid id.
+  // or below the row maximum; -inf when no slot holds a valid id.  The slots
+  // are chosen first (their ids read back from LDS); the dot products then
+  // run together, one pass over the hidden dimension whose W loads carry no
+  // branch (a slot without a valid id reads row 0 and is ignored), so the
+  // scattered rows' round trips to memory overlap instead of following one
+  // another.
   if (active && a.fast && a.need_grad) {
     const float *lg = a.topk_logit + t * K;
     const int R = K < SHIFT_SLOTS ? K : SHIFT_SLOTS;
-    const int dq = a.d / 8;
-    const u32x4 *h16 = reinterpret_cast<const u32x4 *>(
-        reinterpret_cast<const uint16_t *>(a.H) + t * a.d);
-    uint32_t taken = 0;  // bit i: slot lane + 64 i already used
-    float best = -INFINITY;
+    uint32_t taken = 0;  // bit i: slot lane + 64 i already chosen
+    int ids[SHIFT_SLOTS];
+#pragma unroll
+    for (int rr = 0; rr < SHIFT_SLOTS; ++rr) ids[rr] = -1;
     for (int rr = 0; rr < R; ++rr) {
       float bv = -INFINITY;
       int bk = INT_MAX;
@@ -113,18 +117,40 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
       }
       if (bk == INT_MAX) break;
       if ((bk & 63) == lane) taken |= 1u << (bk >> 6);
-      const int id = a.topk_idx[t * K + bk];
-      if (id < 0 || id >= a.V) continue;
-      const u32x4 *w16 = reinterpret_cast<const u32x4 *>(
-          reinterpret_cast<const uint16_t *>(a.W) + (int64_t)id * a.d);
-      float acc = 0.f;
-      for (int c = lane; c < dq; c += 64) {
-        const u32x4 hv = h16[c], wv = w16[c];
+      const int id = s_ids[wave][bk];  // INT_MAX: not a valid id
+#pragma unroll
+      for (int s = 0; s < SHIFT_SLOTS; ++s)
+        if (s == rr) ids[s] = id == INT_MAX ? -1 : id;
+    }
+    const int dq = a.d / 8;
+    const u32x4 *h16 = reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const uint16_t *>(a.H) + t * a.d);
+    const u32x4 *w16[SHIFT_SLOTS];
+#pragma unroll
+    for (int s = 0; s < SHIFT_SLOTS; ++s)
+      w16[s] = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.W) +
+                                               (int64_t)(ids[s] < 0 ? 0 : ids[s]) * a.d);
+    float acc[SHIFT_SLOTS];
+#pragma unroll
+    for (int s = 0; s < SHIFT_SLOTS; ++s) acc[s] = 0.f;
+#pragma unroll 2
+    for (int c = lane; c < dq; c += 64) {
+      const u32x4 hv = h16[c];
+      u32x4 wv[SHIFT_SLOTS];
+#pragma unroll
+      for (int s = 0; s < SHIFT_SLOTS; ++s) wv[s] = w16[s][c];
+#pragma unroll
+      for (int s = 0; s < SHIFT_SLOTS; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc = fmaf(bf16_hi(hv[e]), bf16_hi(wv[e]), fmaf(bf16_lo(hv[e]), bf16_lo(wv[e]), acc));
-      }
-      best = fmaxf(best, wave_sum(acc));
+          acc[s] = fmaf(bf16_hi(hv[e]), bf16_hi(wv[s][e]),
+                        fmaf(bf16_lo(hv[e]), bf16_lo(wv[s][e]), acc[s]));
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SHIFT_SLOTS; ++s) {
+      const float z = wave_sum(acc[s]);
+      if (ids[s] >= 0) best = fmaxf(best, z);
     }
     if (lane == 0) {
       a.shift[r] = best * a.s2;
