@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
     for (int k = lane; k < K; k += 64) {
       const int idk = s_ids[wave][k];
       int rank = 0;
+#pragma unroll 8
       for (int j = 0; j < K; ++j) {
         const int idj = s_ids[wave][j];
         rank += (idj < idk) || (idj == idk && j < k);
@@ -174,15 +175,18 @@ __global__ __launch_bounds__(256) void k_prep_rows(SliceArgs a) {
   }
   __syncthreads();
   if (active) {
-    for (int j = lane; j < a.nseg; j += 64) {
-      const int lo = j * SEG;
-      int L = 0, R = K;
-      while (L < R) {
-        const int mid = (L + R) >> 1;
-        if (s_sorted[wave][mid] < lo) L = mid + 1; else R = mid;
-      }
-      a.first[(size_t)r * a.nseg + j] =
-          int16_t((L < K && s_sorted[wave][L] < lo + SEG) ? L : -1);
+    // first sorted position per segment: -1 everywhere, then, in sorted
+    // order, the position where the ids enter a new segment (invalid ids,
+    // INT_MAX, sort last and are skipped).  The wait orders this wave's
+    // -1 stores before its position stores to the same entries.
+    int16_t *fr = a.first + (size_t)r * a.nseg;
+    for (int j = lane; j < a.nseg; j += 64) fr[j] = int16_t(-1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int k = lane; k < K; k += 64) {
+      const int id = s_sorted[wave][k];
+      if (id == INT_MAX) continue;
+      const int seg = id / SEG;
+      if (k == 0 || s_sorted[wave][k - 1] / SEG != seg) fr[seg] = int16_t(k);
     }
   }
 }
