@@ -198,10 +198,14 @@ __device__ __forceinline__ void row_stats(const SliceArgs &a, int r, int lane, f
                                           float &log2s) {
   const float *mrow = a.mseg + (size_t)r * a.nseg;
   const float *srow = a.sseg + (size_t)r * a.nseg;
+  // (unrolled so that several iterations' loads are in flight; the sums
+  // keep their order)
   mx = -INFINITY;
+#pragma unroll 4
   for (int j = lane; j < a.nseg; j += 64) mx = fmaxf(mx, mrow[j]);
   mx = wave_max(mx);
   float s = 0.f;
+#pragma unroll 4
   for (int j = lane; j < a.nseg; j += 64) s += srow[j] * exp2f(mrow[j] - mx);
   log2s = log2f(wave_sum(s));
 }
