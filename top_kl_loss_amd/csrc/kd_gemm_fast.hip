@@ -14,7 +14,7 @@
 // mn index contiguous (transposing LDS reads), so neither needs a
 // transposed copy.
 //
-// The tile machinery (4-wave and 8-wave tiles, DMA operand copies, swizzled
+// The tile machinery (4-wave tiles, DMA operand copies, swizzled
 // LDS layouts, MFMA schedules) is in kd_mfma_tile.h.
 #include <stdint.h>
 
