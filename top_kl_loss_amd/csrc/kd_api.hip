@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kd_internal.h"
@@ -496,7 +497,7 @@ namespace {
 
 struct DivLayout {
   size_t o_scal, o_rowloss, o_gk, o_k0, o_k1, o_v0, o_v1, o_hist, o_seg, o_units, o_parts,
-      o_partial, total;
+      o_partial, o_bsum, total;
 };
 
 DivLayout make_div_layout(int64_t T, int64_t d, int64_t V, int32_t K) {
@@ -518,6 +519,8 @@ DivLayout make_div_layout(int64_t T, int64_t d, int64_t V, int32_t K) {
   L.o_units = take(sizeof(int32_t) * ((size_t)V + 1));
   L.o_parts = take(sizeof(int32_t) * ((size_t)V + 1));
   L.o_partial = take(sizeof(float) * pmax * (size_t)d);
+  const int64_t nscan = std::max<int64_t>(256 * (int64_t)nblk, V + 1);
+  L.o_bsum = take(sizeof(int32_t) * (size_t)kd::div_scan_blocks(nscan));
   L.total = o;
   return L;
 }
@@ -581,6 +584,7 @@ int kd_topk_div_fwd_bwd(int32_t kind, const void *H, const void *W, kd_dtype dty
   a.unit_start = reinterpret_cast<int32_t *>(ws + L.o_units);
   a.part_start = reinterpret_cast<int32_t *>(ws + L.o_parts);
   a.partial = reinterpret_cast<float *>(ws + L.o_partial);
+  a.bsum = reinterpret_cast<int32_t *>(ws + L.o_bsum);
   hipError_t e = logged(KD_KERNEL_VALID_COUNT, s, [&] {
     return kd::launch_valid_count(mask, (int)T, tau, nullptr, scal, s);
   });

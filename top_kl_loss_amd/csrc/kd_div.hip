@@ -232,8 +232,9 @@ __global__ __launch_bounds__(256) void k_radix_hist(const int32_t *keys, int64_t
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
 }
 
-// Exclusive scan of n int32 in place (one workgroup of 1024 threads, each a
-// contiguous run), total written to *total when not null.
+// Exclusive scan of n int32 in place by one workgroup of 1024 threads, each
+// a contiguous run, total written to *total when not null: for the short
+// list of tile sums of scan_excl below.
 __global__ __launch_bounds__(1024) void k_scan_excl(int32_t *x, int64_t n, int32_t *total) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
@@ -256,6 +257,66 @@ __global__ __launch_bounds__(1024) void k_scan_excl(int32_t *x, int64_t n, int32
     run += v;
   }
   if (total && tid == 1023) *total = part[1023];
+}
+
+// Exclusive scan of n int32 in place over tiles of SCAN_TILE: the tiles'
+// sums (coalesced loads, one tile per workgroup), an exclusive scan of the
+// sums, then each tile scanned with its offset (integer: the result is the
+// plain prefix sum).
+__global__ __launch_bounds__(256) void k_scan_sums(const int32_t *x, int64_t n, int32_t *bsum) {
+  __shared__ int32_t ws[4];
+  const int tid = threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * SCAN_TILE;
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_TILE / 256; ++i) {
+    const int64_t j = b0 + i * 256 + tid;
+    if (j < n) s += x[j];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((tid & 63) == 0) ws[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) bsum[blockIdx.x] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
+__global__ __launch_bounds__(256) void k_scan_apply(int32_t *x, int64_t n, const int32_t *bsum) {
+  constexpr int PER = SCAN_TILE / 256;  // contiguous values per thread
+  __shared__ int32_t ws[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t j0 = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)tid * PER;
+  int32_t v[PER];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    v[i] = j0 + i < n ? x[j0 + i] : 0;
+    s += v[i];
+  }
+  // exclusive prefix of this thread's run within the tile
+  int32_t inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  int32_t run = bsum[blockIdx.x] + inc - s;
+  for (int w = 0; w < wave; ++w) run += ws[w];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (j0 + i < n) x[j0 + i] = run;
+    run += v[i];
+  }
+}
+
+hipError_t scan_excl(int32_t *x, int64_t n, int32_t *bsum, hipStream_t s) {
+  const int64_t nb = div_scan_blocks(n);
+  hipLaunchKernelGGL(k_scan_sums, dim3((unsigned)nb), dim3(256), 0, s, x, n, bsum);
+  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, bsum, nb, (int32_t *)nullptr);
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(256), 0, s, x, n,
+                     (const int32_t *)bsum);
+  return hipGetLastError();
 }
 
 // Stable scatter of one radix pass: each block walks its keys in order, 256
@@ -417,8 +478,7 @@ hipError_t launch_div(const DivArgs &a, hipStream_t s) {
     const int shift = ps * RADIX_BITS;
     hipLaunchKernelGGL(k_radix_hist, dim3(nblk), dim3(256), 0, s, a.keys[cur], n, shift, a.hist,
                        nblk);
-    hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, a.hist, (int64_t)RADIX * nblk,
-                       (int32_t *)nullptr);
+    scan_excl(a.hist, (int64_t)RADIX * nblk, a.bsum, s);
     hipLaunchKernelGGL(k_radix_scatter, dim3(nblk), dim3(256), 0, s, a.keys[cur], a.vals[cur],
                        a.keys[cur ^ 1], a.vals[cur ^ 1], n, shift, a.hist, nblk);
     cur ^= 1;
@@ -426,10 +486,8 @@ hipError_t launch_div(const DivArgs &a, hipStream_t s) {
   const int gv = (a.V + 1 + 255) / 256;
   hipLaunchKernelGGL(k_div_segments, dim3(gv), dim3(256), 0, s, a, a.keys[cur]);
   hipLaunchKernelGGL(k_div_units, dim3(gv), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, a.unit_start, (int64_t)a.V + 1,
-                     (int32_t *)nullptr);
-  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, a.part_start, (int64_t)a.V + 1,
-                     (int32_t *)nullptr);
+  scan_excl(a.unit_start, (int64_t)a.V + 1, a.bsum, s);
+  scan_excl(a.part_start, (int64_t)a.V + 1, a.bsum, s);
   const int64_t max_units = n / DIV_UNIT + a.V;
   const int gw = (int)((max_units + ROWS - 1) / ROWS);
   if (bf16)

@@ -204,7 +204,12 @@ struct DivArgs {
   int32_t *unit_start;      // [V + 1] units per id, then their first index
   int32_t *part_start;      // [V + 1] partial rows per id, then first row
   float *partial;           // [2 ceil(T K / DIV_UNIT), d] partial dW rows
+  int32_t *bsum;            // [div_scan_blocks] tile sums of the scans
 };
+// Tiles of the exclusive scans of the divergence path (RADIX * blocks and
+// V + 1 counts) and the block-sum entries a scan of n values needs.
+constexpr int SCAN_TILE = 4096;
+inline int64_t div_scan_blocks(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
 int radix_passes(int64_t V);
 hipError_t launch_div(const DivArgs &a, hipStream_t s);
 
