@@ -33,6 +33,11 @@
  *   library allocates nothing and keeps no state between calls, apart from
  *   the optional, per-thread measurement hook kd_set_launch_log and the
  *   fixed per-GPU scratch of kd_topk_kl_fwd_noalloc.
+ * - H and W, and the dH and dW outputs, start on a 16-byte boundary (the
+ *   kernels move their rows 16 bytes at a time; any HIP or torch
+ *   allocation qualifies, and since d % 8 == 0 so does every row of one);
+ *   other pointers need only their element's alignment.  A misaligned H,
+ *   W, dH or dW is KD_ERR_INVALID_ARG.
  * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *   the default stream).  Outputs are valid once that stream has
  *   synchronised.  No call synchronises the host.

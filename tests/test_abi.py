@@ -80,9 +80,9 @@ def test_workspace_size_rejects(args, code):
 
 def _call(**kw):
     lib = kd.load_library()
-    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
-             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, loss=1,
-             row_loss=None, dH=1, dW=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a = dict(H=256, W=256, dtype=kd.KD_BF16, idx=256, logit=256, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, loss=256,
+             row_loss=None, dH=256, dW=256, ws=256, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.kd_topk_kl_fwd_bwd(
         a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
@@ -112,6 +112,11 @@ def _call(**kw):
     (dict(ws=None), kd.KD_ERR_WORKSPACE),
     (dict(ws_bytes=100), kd.KD_ERR_WORKSPACE),
     (dict(ws=256 + 16), kd.KD_ERR_WORKSPACE),
+    # H, W, dH, dW must start on a 16-byte boundary
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),
+    (dict(W=256 + 8), kd.KD_ERR_INVALID_ARG),
+    (dict(dH=256 + 4), kd.KD_ERR_INVALID_ARG),
+    (dict(dW=256 + 12), kd.KD_ERR_INVALID_ARG),
 ])
 def test_fwd_bwd_rejects_before_any_hip_call(kw, code):
     assert _call(**kw) == code
@@ -148,8 +153,8 @@ def test_teacher_workspace_size_rejects(args, code):
 
 def _tk_call(**kw):
     lib = kd.load_library()
-    a = dict(H=1, W=1, dtype=kd.KD_BF16, T=256, d=512, V=8192, K=100,
-             chunk=64, idx=1, logit=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a = dict(H=256, W=256, dtype=kd.KD_BF16, T=256, d=512, V=8192, K=100,
+             chunk=64, idx=256, logit=256, ws=256, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.kd_teacher_topk(a["H"], a["W"], a["dtype"], a["T"], a["d"],
                                a["V"], a["K"], a["chunk"], a["idx"],
@@ -157,6 +162,8 @@ def _tk_call(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),  # 16-byte alignment
+    (dict(W=256 + 4), kd.KD_ERR_INVALID_ARG),
     (dict(H=None), kd.KD_ERR_INVALID_ARG),
     (dict(W=None), kd.KD_ERR_INVALID_ARG),
     (dict(idx=None), kd.KD_ERR_INVALID_ARG),
@@ -177,8 +184,8 @@ def test_teacher_topk_rejects_before_any_hip_call(kw, code):
 # ------------------------------------------ split forward / backward, cast
 def _fwd_call(**kw):
     lib = kd.load_library()
-    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
-             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=1, row_loss=None,
+    a = dict(H=256, W=256, dtype=kd.KD_BF16, idx=256, logit=256, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=256, row_loss=None,
              lse=None, ws=256, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.kd_topk_kl_fwd(
@@ -189,9 +196,9 @@ def _fwd_call(**kw):
 
 def _bwd_call(**kw):
     lib = kd.load_library()
-    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
-             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, g=None, dH=1,
-             dW=1, ws=256, ws_bytes=1 << 40, stream=None)
+    a = dict(H=256, W=256, dtype=kd.KD_BF16, idx=256, logit=256, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, flags=0, g=None, dH=256,
+             dW=256, ws=256, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.kd_topk_kl_bwd(
         a["H"], a["W"], a["dtype"], a["idx"], a["logit"], a["mask"], a["T"],
@@ -200,6 +207,8 @@ def _bwd_call(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),  # 16-byte alignment
+    (dict(W=256 + 4), kd.KD_ERR_INVALID_ARG),
     (dict(H=None), kd.KD_ERR_INVALID_ARG),
     (dict(loss=None), kd.KD_ERR_INVALID_ARG),
     (dict(tau=0.0), kd.KD_ERR_INVALID_ARG),
@@ -213,6 +222,8 @@ def test_fwd_rejects_before_any_hip_call(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),  # 16-byte alignment
+    (dict(W=256 + 4), kd.KD_ERR_INVALID_ARG),
     (dict(W=None), kd.KD_ERR_INVALID_ARG),
     (dict(dH=None), kd.KD_ERR_INVALID_ARG),
     (dict(dW=None), kd.KD_ERR_INVALID_ARG),
@@ -272,8 +283,8 @@ def test_entropy_filter_workspace_size():
 
 def _fwd_noalloc_call(**kw):
     lib = kd.load_library()
-    a = dict(H=1, W=1, dtype=kd.KD_BF16, idx=1, logit=1, mask=None, T=256,
-             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=1, row_loss=None,
+    a = dict(H=256, W=256, dtype=kd.KD_BF16, idx=256, logit=256, mask=None, T=256,
+             d=512, V=8192, K=100, tau=1.0, chunk=64, loss=256, row_loss=None,
              lse=None, stream=None)
     a.update(kw)
     return lib.kd_topk_kl_fwd_noalloc(
@@ -290,6 +301,8 @@ def _noalloc_bytes(T, V, K, chunk):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),  # 16-byte alignment
+    (dict(W=256 + 4), kd.KD_ERR_INVALID_ARG),
     (dict(H=None), kd.KD_ERR_INVALID_ARG),
     (dict(loss=None), kd.KD_ERR_INVALID_ARG),
     (dict(tau=-1.0), kd.KD_ERR_INVALID_ARG),
@@ -314,9 +327,9 @@ def test_fwd_noalloc_scratch_bound_covers_the_benchmark_sizes():
 
 def _div_call(**kw):
     lib = kd.load_library()
-    a = dict(kind=kd.KD_DIV_REVERSE_KL, H=1, W=1, dtype=kd.KD_BF16, idx=1,
-             logit=1, mask=None, T=256, d=512, V=8192, K=100, tau=1.0, flags=0,
-             loss=1, row_loss=None, dH=1, dW=1, ws=256, ws_bytes=1 << 40,
+    a = dict(kind=kd.KD_DIV_REVERSE_KL, H=256, W=256, dtype=kd.KD_BF16, idx=256,
+             logit=256, mask=None, T=256, d=512, V=8192, K=100, tau=1.0, flags=0,
+             loss=256, row_loss=None, dH=256, dW=256, ws=256, ws_bytes=1 << 40,
              stream=None)
     a.update(kw)
     return lib.kd_topk_div_fwd_bwd(
@@ -326,6 +339,8 @@ def _div_call(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(H=256 + 2), kd.KD_ERR_INVALID_ARG),  # 16-byte alignment
+    (dict(W=256 + 4), kd.KD_ERR_INVALID_ARG),
     (dict(kind=0), kd.KD_ERR_INVALID_ARG),
     (dict(kind=3), kd.KD_ERR_INVALID_ARG),
     (dict(H=None), kd.KD_ERR_INVALID_ARG),

@@ -63,6 +63,9 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The kernels move rows of H, W, dH and dW 16 bytes at a time.
+bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 int check_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
                 kd_dtype dtype) {
   if (T < 1 || d < 1 || V < 1 || K < 1 || chunk < 1 || K > V)
@@ -323,7 +326,8 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
                        int32_t K, float tau, int32_t chunk, uint32_t flags,
                        float *loss, float *row_loss, float *dH, float *dW,
                        void *workspace, size_t workspace_bytes, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW)
+  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW || misaligned16(H) ||
+      misaligned16(W) || misaligned16(dH) || misaligned16(dW))
     return KD_ERR_INVALID_ARG;
   return run_loss(MODE_FWD_BWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
                   tau, chunk, flags, nullptr, loss, row_loss, nullptr, dH, dW,
@@ -336,7 +340,8 @@ int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
                    int32_t K, float tau, int32_t chunk, float *loss,
                    float *row_loss, float *lse, void *workspace,
                    size_t workspace_bytes, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit || !loss) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || !loss || misaligned16(H) || misaligned16(W))
+    return KD_ERR_INVALID_ARG;
   return run_loss(MODE_FWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
                   tau, chunk, 0u, nullptr, loss, row_loss, lse, nullptr, nullptr,
                   workspace, workspace_bytes, stream);
@@ -390,7 +395,8 @@ int kd_topk_kl_fwd_noalloc(const void *H, const void *W, kd_dtype dtype,
                            const uint8_t *mask, int64_t T, int64_t d, int64_t V,
                            int32_t K, float tau, int32_t chunk, float *loss,
                            float *row_loss, float *lse, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit || !loss) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || !loss || misaligned16(H) || misaligned16(W))
+    return KD_ERR_INVALID_ARG;
   if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
   const int st = check_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
@@ -411,7 +417,9 @@ int kd_topk_kl_bwd(const void *H, const void *W, kd_dtype dtype,
                    int32_t K, float tau, int32_t chunk, uint32_t flags,
                    const float *grad_loss, float *dH, float *dW, void *workspace,
                    size_t workspace_bytes, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit || !dH || !dW) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || !dH || !dW || misaligned16(H) || misaligned16(W) ||
+      misaligned16(dH) || misaligned16(dW))
+    return KD_ERR_INVALID_ARG;
   return run_loss(MODE_BWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
                   tau, chunk, flags, grad_loss, nullptr, nullptr, nullptr, dH, dW,
                   workspace, workspace_bytes, stream);
@@ -441,7 +449,8 @@ int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
                     int64_t d, int64_t V, int32_t K, int32_t chunk,
                     int32_t *topk_idx, float *topk_logit, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  if (!H || !W || !topk_idx || !topk_logit) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || misaligned16(H) || misaligned16(W))
+    return KD_ERR_INVALID_ARG;
   const int st = check_tk_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
   const TkLayout L = make_tk_layout(T, d, V, chunk, dtype);
@@ -543,7 +552,9 @@ int kd_topk_div_fwd_bwd(int32_t kind, const void *H, const void *W, kd_dtype dty
                         float tau, uint32_t flags, float *loss, float *row_loss, float *dH,
                         float *dW, void *workspace, size_t workspace_bytes, void *stream) {
   if (kind != KD_DIV_REVERSE_KL && kind != KD_DIV_JSD) return KD_ERR_INVALID_ARG;
-  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW) return KD_ERR_INVALID_ARG;
+  if (!H || !W || !topk_idx || !topk_logit || !loss || !dH || !dW || misaligned16(H) ||
+      misaligned16(W) || misaligned16(dH) || misaligned16(dW))
+    return KD_ERR_INVALID_ARG;
   if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_INVALID_ARG;
   if (flags & ~uint32_t(KD_FLAG_ACCUMULATE_DW)) return KD_ERR_INVALID_ARG;
   const int st = check_sizes(T, d, V, K, 1, dtype);
