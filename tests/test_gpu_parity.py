@@ -216,3 +216,23 @@ def test_concurrent_calls_on_two_streams():
     for got, want in ((outs[0], ref_a), (outs[1], ref_b)):
         for u, v in zip(got, want):
             assert torch.equal(u, v)
+
+
+def test_misaligned_matrix_is_rejected_before_any_work():
+    # a view that starts 2 bytes into its storage: the library moves rows of
+    # H and W 16 bytes at a time and rejects such a pointer up front
+    import torch
+    import top_kl_loss_amd as kd
+    x = synth.make_case("misaligned", case=42, T=64, d=64, V=512, K=8,
+                        dtype="bf16", chunk=64)
+    dev = G.to_device(x)
+    flat = torch.empty(x.T * x.d + 1, dtype=torch.bfloat16, device="cuda")
+    H = flat[1:].view(x.T, x.d)
+    H.copy_(dev["H"])
+    assert H.data_ptr() % 16 == 2
+    with pytest.raises(kd.KdError) as err:
+        kd.kd_topk_kl_fwd_bwd(H, dev["W"], dev["topk_idx"], dev["topk_logit"],
+                              None, 1.0, 64)
+    assert err.value.status == kd.KD_ERR_INVALID_ARG
+    # the same values at an aligned address run and match the oracle
+    check_case(x)
