@@ -115,7 +115,7 @@ def test_autograd_divergences():
 
 @pytest.mark.parametrize("kind", KINDS)
 def test_t4k_full_size(kind):
-    # the survey's T = 4096, d = 2880, V = 201088, K = 100 bf16 workload: every
+    # the t4k workload (T = 4096, d = 2880, V = 201088, K = 100, bf16): every
     # row's divergence, all of dH and all of dW against the oracle (dense
     # fp64, ~30 s of host time)
     import torch

@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, against the whole fp64 oracle.
 
 For every full-size workload the library runs at each slice size named for
-it (the benchmark's and the survey's), its outputs are copied to the host,
+it (the benchmark's and the smaller ones), its outputs are copied to the host,
 and the oracle is evaluated over the same batch slice by slice (1024 token
 rows at a time, with the batch's valid-token count; chunk invariance is one
 of the oracle's pins).  Every row's KL and every dH row are compared as the
@@ -157,8 +157,9 @@ def test_t8k_masked_all_rows_and_dw():
     _RUNS.clear()
 
 
-# -------------------------------------------------------------- t32k (c4)
-# slices of 8192 (the benchmark's), 1024 (the survey's) and 16384 (the
+# ------------------------------------------------------------------ t32k
+# slices of 8192 (the benchmark's), 1024 (a small slice: dW in groups of
+# two) and 16384 (the
 # slice's probability buffer, 16384 x 201216 bf16 = 6.6 GB, exceeds the
 # 4 GiB reach of 32-bit buffer offsets: tiles address it from their own
 # first row)
