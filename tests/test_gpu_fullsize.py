@@ -137,7 +137,7 @@ def _blocks(T):
     return [(r0, min(T, r0 + BLOCK_ROWS)) for r0 in range(0, T, BLOCK_ROWS)]
 
 
-# --------------------------------------------------------------- t4k (c2)
+# --------------------------------------------------------------------- t4k
 def test_t4k_all_rows_and_dw():
     # T = 4096, d = 2880, V = 201088, slices of 1024; also the forward-only
     # entry point
@@ -147,7 +147,7 @@ def test_t4k_all_rows_and_dw():
     _RUNS.clear()
 
 
-# --------------------------------------------------------------- t8k (c3)
+# --------------------------------------------------------------------- t8k
 def test_t8k_masked_all_rows_and_dw():
     # 5% padding (410 rows), slices of 1024
     r = _run("t8k", (1024,))
@@ -184,7 +184,7 @@ def test_t32k_loss_and_dw():
     _RUNS.clear()
 
 
-# ------------------------------------------------------- t32k_d4096 (c5)
+# ------------------------------------------------------------ t32k_d4096
 # d = 4096, V = 151936, tau = 2, teacher logits x 0.5, 15% padding; the
 # slice-size sweep 512 ... 4096, every size against the oracle
 D4096_CHUNKS = synth.CHUNK_SWEEP["t32k_d4096"]
