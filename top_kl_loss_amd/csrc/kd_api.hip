@@ -102,8 +102,9 @@ Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
     if (g > nsl) g = nsl;
     L.G = (int)g;
   }
-  L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;  // dW: 192 x 320 tiles when 320
-  L.dh_bn = 256;                                   // dH: 256 x 256 tiles
+  // dH and dW: 256 x 320 tiles when d is a multiple of 320, else 256 x 256
+  L.dw_bn = L.fast ? kd::fast_bn((int)d) : 256;
+  L.dh_bn = L.dw_bn;
   L.splits = kd::dh_splits(L.C, (int)d, L.nseg, L.fast, L.dh_bn);
   L.esize = dtype == KD_BF16 ? 2 : 4;
   const size_t C = L.C, nseg = L.nseg;

@@ -238,41 +238,42 @@ void k_fast_logits_redo(SliceArgs a) {
 // On 4-wave tiles, both operands copied by DMA:
 //  dH partials = P~ W per vocabulary split (f applied by the reduction),
 //  A = P~ (K-contiguous), B = W (MN-contiguous: vocabulary rows, hidden
-//  contiguous), 256 x 256 tiles;
+//  contiguous);
 //  dW (+)= P~^T (f H_c), A = P~ (MN-contiguous: token rows, vocabulary
-//  contiguous), B = (f H_c)^T (K-contiguous), 192 x 320 tiles when d is a
-//  multiple of 320 (no N padding; d = 2880 = 9 x 320), else 256 x 256.
+//  contiguous), B = (f H_c)^T (K-contiguous);
+//  both on 256 x 320 tiles when d is a multiple of 320 (no N padding;
+//  d = 2880 = 9 x 320), else 256 x 256.
+template <class S>
 __global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fast_dh4(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nmt = (a.C + BM - 1) / BM;
-  const int nnt = (a.d + BN - 1) / BN;
+  const int nmt = (a.C + S::RA - 1) / S::RA;
+  const int nnt = (a.d + S::RB - 1) / S::RB;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int split = tile / (nnt * nmt);
   int mt, nt;
   group_tile(tile % (nnt * nmt), nmt, nnt, 4, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int m0 = mt * S::RA, n0 = nt * S::RB;
   const int sbeg = (int)((int64_t)split * a.nseg / a.splits);
   const int send = (int)((int64_t)(split + 1) * a.nseg / a.splits);
-  using S = w4::SquareBMN;
   w4::Copy<S::RA> ca;
   w4::CopyMN<S::RB> cb;
   ca.init(a.P, (uint64_t)a.C * a.ldp * 2, a.ldp, m0, wave, lane);
   cb.init(a.W, (uint64_t)a.V * a.d * 2, a.d, n0, wave, lane);
-  f32x4 acc[8][8];
+  f32x4 acc[S::TMB][S::TNB];
   w4::nt_loop<S>(ca, cb, sbeg * SEG, (send - sbeg) * (SEG / BK), lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
   float *out = a.dh_part + (size_t)split * a.dh_stride;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < S::TMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = n0 + wn * 128 + w4::acc_col4(j, lane);
+    for (int j = 0; j < S::TNB; ++j) {
+      const int col = n0 + wn * 16 * S::TNB + w4::acc_col4(j, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 128 + w4::acc_row4(i, e, lane);
+        const int row = m0 + wm * 16 * S::TMB + w4::acc_row4(i, e, lane);
         if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
       }
     }
@@ -409,9 +410,15 @@ hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
   return launch(k_fast_logits, ((a.C + BM - 1) / BM) * a.nseg, a, s, w4::Square::LDS, w4::NT);
 }
 
+template <class S>
+hipError_t launch_dh(const SliceArgs &a, hipStream_t s) {
+  const int tiles = ((a.C + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB) * a.splits;
+  return launch(k_fast_dh4<S>, tiles, a, s, S::LDS, w4::NT);
+}
+
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s) {
-  const int tiles = ((a.C + BM - 1) / BM) * ((a.d + BN - 1) / BN) * a.splits;
-  return launch(k_fast_dh4, tiles, a, s, w4::SquareBMN::LDS, w4::NT);
+  if (a.dh_bn == w4::WideBMN::RB) return launch_dh<w4::WideBMN>(a, s);
+  return launch_dh<w4::SquareBMN>(a, s);
 }
 
 hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
@@ -428,15 +435,15 @@ hipError_t launch_flagged_rows(const SliceArgs &a, hipStream_t s) {
   return launch_fix_flagged(a, s);
 }
 
-hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
-  if (a.dw_bn == w4::TallAMN::RB) {
-    using S = w4::TallAMN;
-    return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
-                  S::LDS, w4::NT);
-  }
-  using S = w4::SquareAMN;
+template <class S>
+hipError_t launch_dw(const SliceArgs &a, hipStream_t s) {
   return launch(k_fast_dw4<S>, ((a.V + S::RA - 1) / S::RA) * ((a.d + S::RB - 1) / S::RB), a, s,
                 S::LDS, w4::NT);
+}
+
+hipError_t launch_fast_dw(const SliceArgs &a, hipStream_t s) {
+  if (a.dw_bn == w4::WideAMN::RB) return launch_dw<w4::WideAMN>(a, s);
+  return launch_dw<w4::SquareAMN>(a, s);
 }
 
 }  // namespace kd

@@ -83,7 +83,7 @@ struct SliceArgs {
   int dw_beta;       // 0: dW = G^T H, 1: dW += G^T H
   int fast;          // use the tuned bf16 kernels
   int need_grad;     // 0: forward only (no P store, no G)
-  int dh_bn, dw_bn;  // tuned path: N-tile width of dH (256) and dW (256 or 320)
+  int dh_bn, dw_bn;  // tuned path: N-tile width of dH and dW (256 or 320)
   float *lse_out;    // [T] row logsumexp of z/tau, or null
 };
 
@@ -98,8 +98,8 @@ constexpr int DW_BM = 128, DW_BN = 128;   // dW:      V x d, K = C
 bool use_fast(bool bf16, int64_t C, int64_t d, int64_t V, int64_t ldp);
 int dh_splits(int C, int d, int nseg, bool fast, int bn);
 int fast_dh_splits(int C, int d, int nseg, int bn);
-// N-tile width (256 or 320) of the tuned dW GEMM for hidden size d: the one
-// that wastes less matrix-core work on padding.
+// N-tile width (256 or 320) of the tuned dH and dW GEMMs for hidden size d:
+// the one that wastes less matrix-core work on padding.
 int fast_bn(int d);
 hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s);
 hipError_t launch_fast_dh(const SliceArgs &a, hipStream_t s);

@@ -1,8 +1,9 @@
 // Matrix-core tile machinery shared by the tuned bf16 GEMMs (gfx950).
 //
 // Workgroups of 4 waves (one per SIMD, namespace w4 below) run the logits,
-// dH and dW products: 128 x 128 (or 96 x 160) wave tiles of
-// v_mfma_f32_16x16x32_bf16 with the accumulators in AGPRs.  On this chip the
+// dH and dW products: 128 x 128 (or 128 x 160) wave tiles of
+// v_mfma_f32_16x16x32_bf16 with the accumulators in AGPRs (those of a
+// 128 x 160 wave tile past the 256 AGPRs in VGPRs).  On this chip the
 // GEMMs run power-limited (the shader clock drops under MFMA load), and
 // these tiles read few LDS bytes per flop and keep the matrix cores busy per
 // clock.
@@ -41,6 +42,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_res(const void *base,
   const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
                                            (int)n, 0x00020000);
+}
+
+// Bytes from `skip` to `bytes` (0 when skip >= bytes), capped at 2^32 - 1, with
+// 32-bit compares only: the scalar unit has no 64-bit ordered compare, and a
+// 64-bit one moves the operands to VGPRs (|bytes - skip| < 2^63 here).
+__device__ __forceinline__ uint32_t bytes_left(uint64_t bytes, uint64_t skip) {
+  const uint64_t rem = bytes - skip;
+  const int32_t hi = (int32_t)(rem >> 32);
+  return hi < 0 ? 0u : (hi > 0 ? 0xffffffffu : (uint32_t)rem);
 }
 
 // Buffer resource over the rows mn0.. of a row-major operand (pitch ld
@@ -133,7 +143,9 @@ __device__ __forceinline__ int mnf(int kr) {
 
 // Tile of 2 x 2 waves, each TMB x TNB blocks of 16 x 16: A has 32 TMB rows,
 // B 32 TNB rows per stage (128 bytes each).  Every half-step reads
-// TMB + TNB = 16 fragments and issues 16 copy instructions per wave.  With
+// TMB + TNB fragments and issues as many copy instructions per wave.  The
+// accumulators of the first 64 blocks (i-major) sit in the 256 AGPRs, those
+// of the rest (at most 16) in VGPRs.  With
 // AIL (A interleaved), wave row wm holds the 16-row blocks i of tile rows
 // 32 i + 16 wm .. + 15 instead of 16 TMB wm + 16 i .. + 15, so that any 32
 // consecutive tile rows come from both wave rows (an epilogue can stage
@@ -153,8 +165,7 @@ struct Shape {
   static constexpr int STB = (RA + RB) * 128;
   static constexpr int LDS = 2 * STB;
   static constexpr int NR = TMB + TNB;
-  static_assert(NR == 16, "16 fragment reads and copy instructions per half-step");
-  static_assert(TMB * TNB * 4 <= 256, "accumulators fit the AGPRs");
+  static_assert(TMB * TNB <= 80, "at most 16 accumulator blocks outside the AGPRs");
   static_assert(!(AIL && AMN), "interleaved A blocks are K-contiguous");
   // MN-contiguous stage rows of P = R / 8 chunks, P a multiple of 8: the
   // XOR of 2 mnf then maps a row's chunks onto themselves
@@ -163,11 +174,16 @@ struct Shape {
 };
 using Square = Shape<8, 8>;   // 256 x 256
 using SquareI = Shape<8, 8, true>;  // 256 x 256, A blocks interleaved
-using Tall = Shape<6, 10>;    // 192 x 320 (N = d multiple of 320)
 using SquareBMN = Shape<8, 8, false, false, true>;  // dH: B = W
-using SquareAMN = Shape<8, 8, false, true, false>;  // dW: A = P~ (d not 320 k)
-using TallAMN = Shape<6, 10, false, true, false>;   // dW: A = P~, 192 x 320
-static_assert(Tall::LDS <= 160 * 1024, "LDS");
+using SquareAMN = Shape<8, 8, false, true, false>;  // dW: A = P~
+using WideBMN = Shape<8, 10, false, false, true>;   // dH, 256 x 320 (N = d multiple of 320)
+using WideAMN = Shape<8, 10, false, true, false>;   // dW, 256 x 320
+static_assert(WideAMN::LDS <= 160 * 1024, "LDS");
+
+// Accumulator block (i, j) of a TNB-wide wave tile sits in AGPRs when its
+// i-major index is below 64 (256 AGPRs), else in VGPRs.
+template <int TNB>
+__device__ __forceinline__ constexpr bool in_agpr(int i, int j) { return i * TNB + j < 64; }
 
 // ROWS rows of a K-contiguous operand, element (mn, k) at byte
 // (mn * ld + k) * 2 of the buffer (the resource starts at row mn0); wave w
@@ -230,7 +246,8 @@ struct CopyMN {
   }
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t res(int k0) const {
     const uint64_t skip = (uint64_t)k0 * ldb;
-    return make_res(base + skip, bytes > skip ? bytes - skip : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base + skip), (short)0,
+                                             (int)bytes_left(bytes, skip), 0x00020000);
   }
   __device__ __forceinline__ void issue(char *tile, int k0, int n) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(res(k0), (lds_vptr)(tile + (w * N + n) * 1024), 16,
@@ -247,11 +264,23 @@ using CopyA = __type_pack_element<S::AMN ? 1 : 0, Copy<S::RA>, CopyMN<S::RA>>;
 template <class S>
 using CopyB = __type_pack_element<S::BMN ? 1 : 0, Copy<S::RB>, CopyMN<S::RB>>;
 
+// acc += a b^T (AG: accumulator in AGPRs, else in VGPRs); mfma_first: acc = a b^T.
+// A VGPR destination must not share registers with the sources: the
+// first MFMA's output is early-clobber (a tied accumulator cannot overlap
+// the other, simultaneously live inputs anyway).
+template <bool AG>
 __device__ __forceinline__ void mfma(f32x4 &acc, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (AG)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+template <bool AG>
 __device__ __forceinline__ void mfma_first(f32x4 &acc, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  if constexpr (AG)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 
 // Byte offset, in an MN-contiguous stage of P chunks per k-row, of the 8
@@ -363,10 +392,18 @@ __device__ __forceinline__ void half_step(f32x4 (&acc)[S::TMB][S::TNB],
 #pragma unroll
     for (int idx = r * NM / S::NR; idx < (r + 1) * NM / S::NR; ++idx) {
       const int i = idx / S::TNB, j = idx % S::TNB;
-      if (FIRST)
-        mfma_first(acc[i][j], fa[i], fb[j]);
-      else
-        mfma(acc[i][j], fa[i], fb[j]);
+      // (both conditions are constants once the loops are unrolled)
+      if (in_agpr<S::TNB>(i, j)) {
+        if (FIRST)
+          mfma_first<true>(acc[i][j], fa[i], fb[j]);
+        else
+          mfma<true>(acc[i][j], fa[i], fb[j]);
+      } else {
+        if (FIRST)
+          mfma_first<false>(acc[i][j], fa[i], fb[j]);
+        else
+          mfma<false>(acc[i][j], fa[i], fb[j]);
+      }
     }
   }
 }
@@ -441,7 +478,12 @@ __device__ __forceinline__ void acc_ready(f32x4 (&acc)[TMB][TNB]) {
 #pragma unroll
   for (int i = 0; i < TMB; ++i)
 #pragma unroll
-    for (int j = 0; j < TNB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    for (int j = 0; j < TNB; ++j) {
+      if (in_agpr<TNB>(i, j))
+        asm volatile("" : "+a"(acc[i][j]));
+      else
+        asm volatile("" : "+v"(acc[i][j]));
+    }
 }
 
 // Position of accumulator element e of block (i, j) in the wave tile (rows:
