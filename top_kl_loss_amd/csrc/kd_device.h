@@ -76,6 +76,26 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int n) {
   return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
 }
 
+// Reductions over each aligned group of 8 consecutive lanes, the result in
+// all 8 (DPP lane moves: swap neighbours, swap pairs within the quad, then
+// mirror within the half row, lane i <- 7 - i).  Every lane of a group ends
+// with the same bits (each step adds two values in either order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  return fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+}
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  return v + dpp_mov<0x141>(v);
+}
+
 // Wave-wide (64-lane) reductions through cross-lane shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

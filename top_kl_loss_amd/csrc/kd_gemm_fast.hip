@@ -61,34 +61,42 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
   const bool grads = MODE == 1 || a.need_grad;
   const int part = tid & 7, pr = tid >> 3;
 
-  // Teacher ids of tile row m0 + tid inside this segment, fetched now so
-  // that their latency hides under the main loop: up to NHIT (column, slot)
-  // pairs; `more` marks rows with further ids.
+  // Teacher ids of tile row m0 + tid inside this segment, fetched during the
+  // main loop so that their latency hides under it: the row's first sorted
+  // position in the segment is loaded with the first k-step's operands, the
+  // next NHIT + 1 sorted ids and NHIT slots once it has landed (no use of
+  // them before the loop ends).  After the loop they become up to NHIT
+  // (column, slot) pairs; `more` marks rows with further ids.
   constexpr int NHIT = 4;
-  int hit_col[NHIT], hit_slot[NHIT];
-  bool more = false;
+  int pos = -1;
+  if (MODE == 0 && m0 + tid < a.C) pos = a.first[(size_t)(m0 + tid) * a.nseg + seg];
+  int id_raw[NHIT + 1], slot_raw[NHIT];
 #pragma unroll
-  for (int q = 0; q < NHIT; ++q) hit_col[q] = -1;
-  if (MODE == 0 && m0 + tid < a.C) {
-    const int r = m0 + tid;
-    const int pos = a.first[(size_t)r * a.nseg + seg];
+  for (int q = 0; q <= NHIT; ++q) id_raw[q] = INT32_MAX;
+#pragma unroll
+  for (int q = 0; q < NHIT; ++q) slot_raw[q] = 0;
+  auto fetch_ids = [&] {
     if (pos >= 0) {
-      const int32_t *sid = a.sid + (size_t)r * a.K;
-      const int32_t *sslot = a.sslot + (size_t)r * a.K;
+      const int32_t *sid = a.sid + (size_t)(m0 + tid) * a.K;
+      const int32_t *sslot = a.sslot + (size_t)(m0 + tid) * a.K;
 #pragma unroll
-      for (int q = 0; q < NHIT; ++q) {
-        const int p = pos + q;
-        const int id = p < a.K ? sid[p] : INT32_MAX;
-        if (id < n0 + SEG) {
-          hit_col[q] = id - n0;
-          hit_slot[q] = sslot[p];
-        }
-      }
-      if (pos + NHIT < a.K && sid[pos + NHIT] < n0 + SEG) more = true;
+      for (int q = 0; q <= NHIT; ++q)
+        if (pos + q < a.K) id_raw[q] = sid[pos + q];
+#pragma unroll
+      for (int q = 0; q < NHIT; ++q)
+        if (pos + q < a.K) slot_raw[q] = sslot[pos + q];
     }
-  }
+  };
   f32x4 acc[8][8];
-  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc);
+  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc, fetch_ids);
+  int hit_col[NHIT], hit_slot[NHIT];
+#pragma unroll
+  for (int q = 0; q < NHIT; ++q) {
+    const bool in = id_raw[q] < n0 + SEG;  // (INT32_MAX past the row's ids)
+    hit_col[q] = in ? id_raw[q] - n0 : -1;
+    hit_slot[q] = slot_raw[q];
+  }
+  const bool more = id_raw[NHIT] < n0 + SEG;
 
   // Shifts of this thread's 8 rows (2 per pass), loaded after the main loop
   // (registers there are full); rows past C store 0 (shift +inf).  MODE 1:
@@ -122,9 +130,15 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
           stage[(ii * 32 + wm * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
                 w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
-    // Rows one at a time (fewer live registers): z of the row (-inf past V:
-    // only the vocabulary's last segment has such columns), the statistics,
-    // and P~ packed to bf16 pairs of adjacent columns.
+    if (tail) {
+      // only the vocabulary's last segment has columns past V: -inf there
+      // (2^(-inf) = 0 excludes them from the statistics and from P~)
+      const int nv = a.V - n0, nx = BN - nv;
+      for (int e = tid; e < 64 * nx; e += w4::NT) stage[(e / nx) * PITCH + nv + e % nx] = -INFINITY;
+      __syncthreads();
+    }
+    // Rows one at a time (fewer live registers): z of the row, the
+    // statistics, and P~ packed to bf16 pairs of adjacent columns.
     const int r0 = m0 + 64 * pass + 2 * pr;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -136,18 +150,17 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
           const int col = j * 8 * TPR + part * 8 + 4 * h;
           const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + (2 * pr + q) * PITCH + col);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[j * 8 + 4 * h + u] = (tail && n0 + col + u >= a.V) ? -INFINITY : z[u];
+          for (int u = 0; u < 4; ++u) v[j * 8 + 4 * h + u] = z[u];
         }
       if (MODE == 0) {
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int c = 0; c < CPT; ++c) m4[c & 3] = fmaxf(m4[c & 3], v[c]);
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-#pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        mx *= s2;  // the segment's shift, base-2 units
-        // P~ = 2^(z s2 - mx) 2^(mx - sh): one scale per row and segment
+        // the segment's maximum, base-2 units (the 8 lanes of a row agree)
+        const float mx = group8_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * s2;
+        // P~ = 2^(z s2 - mx) 2^(mx - sh): one scale per row and segment (the
+        // statistics do not depend on the shift, so a forward-only call
+        // gets the same bits)
         const float cq = __builtin_amdgcn_exp2f(mx - sh[pass][q]);
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -157,9 +170,7 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
           s4[c & 3] += pv;
           v[c] = pv * cq;
         }
-        float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-#pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        const float sum = group8_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
         if (part == 0 && r0 + q < a.C) {
           a.mseg[(size_t)(r0 + q) * a.nseg + seg] = mx;
           a.sseg[(size_t)(r0 + q) * a.nseg + seg] = sum;
@@ -243,6 +254,53 @@ void k_fast_logits_redo(SliceArgs a) {
 //  contiguous), B = (f H_c)^T (K-contiguous);
 //  both on 256 x 320 tiles when d is a multiple of 320 (no N padding;
 //  d = 2880 = 9 x 320), else 256 x 256.
+// A wave's accumulators to out[row * ld + col] (fp32, rows < nrows and
+// columns < ncols kept), stored or (ADD) atomically added.  A tile inside
+// both bounds (`full`, wave-uniform) takes one row pointer per accumulator
+// row and the column blocks at immediate offsets, with no per-element
+// checks.
+template <class S, bool ADD>
+__device__ __forceinline__ void tile_out(float *out, int64_t ld, bool full, int nrows, int ncols,
+                                         int m0, int n0, int wm, int wn, int lane,
+                                         f32x4 (&acc)[S::TMB][S::TNB]) {
+  const int row0 = m0 + wm * 16 * S::TMB + w4::acc_row4(0, 0, lane);
+  const int col0 = n0 + wn * 16 * S::TNB + w4::acc_col4(0, lane);
+  if (full) {
+    float *base = out + (size_t)row0 * ld + col0;
+#pragma unroll
+    for (int i = 0; i < S::TMB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float *p = base + (size_t)(16 * i + e) * ld;
+#pragma unroll
+        for (int j = 0; j < S::TNB; ++j) {
+          if (ADD)
+            unsafeAtomicAdd(p + 16 * j, acc[i][j][e]);
+          else
+            p[16 * j] = acc[i][j][e];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < S::TMB; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TNB; ++j) {
+      const int col = col0 + 16 * j;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + 16 * i + e;
+        if (row < nrows && col < ncols) {
+          float *p = out + (size_t)row * ld + col;
+          if (ADD)
+            unsafeAtomicAdd(p, acc[i][j][e]);
+          else
+            *p = acc[i][j][e];
+        }
+      }
+    }
+}
+
 template <class S>
 __global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fast_dh4(SliceArgs a) {
@@ -266,17 +324,8 @@ void k_fast_dh4(SliceArgs a) {
   w4::nt_loop<S>(ca, cb, sbeg * SEG, (send - sbeg) * (SEG / BK), lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
   float *out = a.dh_part + (size_t)split * a.dh_stride;
-#pragma unroll
-  for (int i = 0; i < S::TMB; ++i)
-#pragma unroll
-    for (int j = 0; j < S::TNB; ++j) {
-      const int col = n0 + wn * 16 * S::TNB + w4::acc_col4(j, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 16 * S::TMB + w4::acc_row4(i, e, lane);
-        if (row < a.C && col < a.d) out[(size_t)row * a.d + col] = acc[i][j][e];
-      }
-    }
+  tile_out<S, false>(out, a.d, m0 + S::RA <= a.C && n0 + S::RB <= a.d, a.C, a.d, m0, n0, wm, wn,
+                     lane, acc);
 }
 
 template <class S>
@@ -298,25 +347,13 @@ void k_fast_dw4(SliceArgs a) {
   f32x4 acc[S::TMB][S::TNB];
   w4::nt_loop<S>(ca, cb, 0, (a.C + BK - 1) / BK, lds, wm, wn, lane, acc);
   w4::acc_ready(acc);
-#pragma unroll
-  for (int i = 0; i < S::TMB; ++i)
-#pragma unroll
-    for (int j = 0; j < S::TNB; ++j) {
-      const int col = n0 + wn * 16 * S::TNB + w4::acc_col4(j, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 16 * S::TMB + w4::acc_row4(i, e, lane);
-        if (row < a.V && col < a.d) {
-          float *p = a.dW + (size_t)row * a.d + col;
-          // exactly one addition per element and slice, slices in stream
-          // order: the result does not depend on timing
-          if (a.dw_beta)
-            unsafeAtomicAdd(p, acc[i][j][e]);
-          else
-            *p = acc[i][j][e];
-        }
-      }
-    }
+  // exactly one addition per element and dW GEMM, the GEMMs in stream
+  // order: the result does not depend on timing
+  const bool full = m0 + S::RA <= a.V && n0 + S::RB <= a.d;
+  if (a.dw_beta)
+    tile_out<S, true>(a.dW, a.d, full, a.V, a.d, m0, n0, wm, wn, lane, acc);
+  else
+    tile_out<S, false>(a.dW, a.d, full, a.V, a.d, m0, n0, wm, wn, lane, acc);
 }
 
 // dst[j * ldd + r] = src[r * d + j] (times rscale[r] when rscale is not

@@ -408,21 +408,29 @@ __device__ __forceinline__ void half_step(f32x4 (&acc)[S::TMB][S::TNB],
   }
 }
 
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
 // Main loop on the two stages s0 and s1 (restrict: the compiler then knows
 // that the copies into one stage and the fragment reads from the other do
 // not overlap, and waits for no copy before a transposing read; the
 // explicit waits below order every copy before the reads of its stage).
 // The loop body is two k-steps, so each access names its stage statically.
-template <class S, class CA, class CB>
+// `hook` runs once the first k-step's operands, and every load the caller
+// issued before the loop, have landed: loads it issues complete during the
+// first k-step (and are waited for at its end).
+template <class S, class CA, class CB, class F>
 __device__ __forceinline__ void nt_loop_stages(CA &ca, CB &cb, int kbeg, int nk,
                                                char *__restrict__ s0, char *__restrict__ s1,
                                                const FragOff<S> &fo,
-                                               f32x4 (&acc)[S::TMB][S::TNB]) {
+                                               f32x4 (&acc)[S::TMB][S::TNB], F &hook) {
   u32x4 fa0[S::TMB], fb0[S::TNB], fa1[S::TMB], fb1[S::TNB];
   ca.issue_all(s0, kbeg);
   cb.issue_all(s0 + S::OPA, kbeg);
   wait_vm0();
   __syncthreads();
+  hook();
 #pragma unroll
   for (int r = 0; r < S::NR; ++r) read_frag<S>(s0, fo, 0, r, fa0, fb0);
   const int k1 = kbeg + (nk > 1 ? 1 : 0) * BK;
@@ -454,16 +462,18 @@ __device__ __forceinline__ void nt_loop_stages(CA &ca, CB &cb, int kbeg, int nk,
 
 // Main loop: acc = A[m0.., kbeg + 64 nk) B[n0.., ...)^T, operands copied by
 // DMA (K- or MN-contiguous as S says); nk >= 1.  On return every copy has
-// landed; callers reusing LDS call __syncthreads first.
-template <class S, class CA, class CB>
+// landed; callers reusing LDS call __syncthreads first.  `hook`: see
+// nt_loop_stages.
+template <class S, class CA, class CB, class F = NoHook>
 __device__ __forceinline__ void nt_loop(CA &ca, CB &cb, int kbeg, int nk, char *lds, int wm,
-                                        int wn, int lane, f32x4 (&acc)[S::TMB][S::TNB]) {
+                                        int wn, int lane, f32x4 (&acc)[S::TMB][S::TNB],
+                                        F hook = F()) {
   const FragOff<S> fo(wm, wn, lane);
   // the second stage's offset is hidden from the compiler: with both stages
   // at constant offsets of one array it drops the restrict information
   int st = S::STB;
   asm volatile("" : "+s"(st));
-  nt_loop_stages<S>(ca, cb, kbeg, nk, lds, lds + st, fo, acc);
+  nt_loop_stages<S>(ca, cb, kbeg, nk, lds, lds + st, fo, acc, hook);
 }
 
 // Wait states between the last MFMA and the first read of its accumulator
