@@ -18,6 +18,8 @@
 // LDS layouts, MFMA schedules) is in kd_mfma_tile.h.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kd_device.h"
 #include "kd_internal.h"
 #include "kd_mfma_tile.h"
@@ -46,8 +48,29 @@ using namespace tile;
 // 64 p + sr.  Thread (pr, part) = (tid / 8, tid % 8) takes the two rows
 // 2 pr and 2 pr + 1 and the 8-column groups part, part + 8, ... of them, so
 // the 8 threads of a row store whole 128-byte lines of P~.
+//
+// The epilogue stages in the LDS above the main loop's first stage, so a
+// workgroup that runs several tiles issues the next tile's first k-step
+// copies (and loads its rows' first teacher positions) before this tile's
+// epilogue, and the next main loop starts on operands already in flight.
+constexpr int LG_STAGE_OFF = w4::SquareI::STB;  // epilogue staging: above stage 0
+constexpr int LG_PITCH = BN + 4;                // fp32 per staged row
+constexpr int LG_LDS = LG_STAGE_OFF + 64 * LG_PITCH * 4;
+static_assert(LG_LDS >= w4::SquareI::LDS && LG_LDS <= 160 * 1024, "LDS");
+
+// First sorted position of tile row m0 + tid's teacher ids in segment seg
+// (-1: none, or no such row).
+__device__ __forceinline__ int first_pos(const SliceArgs &a, int mt, int seg) {
+  const int r = mt * BM + (int)threadIdx.x;
+  return r < a.C ? a.first[(size_t)r * a.nseg + seg] : -1;
+}
+
+// Tile (mt, seg); `issued`: its first k-step's copies are in flight into
+// stage 0 and `pos` holds first_pos (MODE 0).  When next_mt >= 0 the next
+// tile's first k-step is issued before the epilogue; returns its first_pos.
 template <int MODE>
-__device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg, char *lds) {
+__device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, char *lds,
+                                           bool issued, int pos, int next_mt, int next_seg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = mt * BM, n0 = seg * SEG;
@@ -68,8 +91,7 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
   // them before the loop ends).  After the loop they become up to NHIT
   // (column, slot) pairs; `more` marks rows with further ids.
   constexpr int NHIT = 4;
-  int pos = -1;
-  if (MODE == 0 && m0 + tid < a.C) pos = a.first[(size_t)(m0 + tid) * a.nseg + seg];
+  if (MODE != 0) pos = -1;
   int id_raw[NHIT + 1], slot_raw[NHIT];
 #pragma unroll
   for (int q = 0; q <= NHIT; ++q) id_raw[q] = INT32_MAX;
@@ -88,7 +110,7 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
     }
   };
   f32x4 acc[8][8];
-  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc, fetch_ids);
+  w4::nt_loop<S>(ca, cb, 0, a.d / BK, lds, wm, wn, lane, acc, fetch_ids, issued);
   int hit_col[NHIT], hit_slot[NHIT];
 #pragma unroll
   for (int q = 0; q < NHIT; ++q) {
@@ -111,11 +133,22 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
       if (grads && r < a.C && (MODE == 0 || a.flag[r])) sh[pass][q] = a.shift[r];
     }
   w4::acc_ready(acc);
+  // every wave is past its last fragment read: stage 0 may be refilled
   __syncthreads();
+  int next_pos = -1;
+  if (next_mt >= 0) {
+    w4::Copy<S::RA> na;
+    w4::Copy<S::RB> nb;
+    na.init(H, (uint64_t)a.C * a.d * 2, a.d, next_mt * BM, wave, lane);
+    nb.init(W, (uint64_t)a.V * a.d * 2, a.d, next_seg * SEG, wave, lane);
+    na.issue_all(lds, 0);
+    nb.issue_all(lds + S::OPA, 0);
+    if (MODE == 0) next_pos = first_pos(a, next_mt, next_seg);
+  }
 
-  constexpr int PITCH = BN + 4;
+  constexpr int PITCH = LG_PITCH;
   constexpr int TPR = 8, CPT = BN / TPR;
-  float *stage = reinterpret_cast<float *>(lds);
+  float *stage = reinterpret_cast<float *>(lds + LG_STAGE_OFF);
   uint16_t *P = reinterpret_cast<uint16_t *>(a.P);
   const float s2 = a.s2;
   const bool tail = n0 + BN > a.V;
@@ -129,13 +162,13 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
         for (int e = 0; e < 4; ++e)
           stage[(ii * 32 + wm * 16 + 4 * (lane >> 4) + e) * PITCH + wn * 128 +
                 w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
-    __syncthreads();
+    lds_barrier();
     if (tail) {
       // only the vocabulary's last segment has columns past V: -inf there
       // (2^(-inf) = 0 excludes them from the statistics and from P~)
       const int nv = a.V - n0, nx = BN - nv;
       for (int e = tid; e < 64 * nx; e += w4::NT) stage[(e / nx) * PITCH + nv + e % nx] = -INFINITY;
-      __syncthreads();
+      lds_barrier();
     }
     // Rows one at a time (fewer live registers): z of the row, the
     // statistics, and P~ packed to bf16 pairs of adjacent columns.
@@ -208,7 +241,7 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
         if (more) {
           const int32_t *sid = a.sid + (size_t)r_own * a.K;
           const int32_t *sslot = a.sslot + (size_t)r_own * a.K;
-          for (int p = a.first[(size_t)r_own * a.nseg + seg] + NHIT; p < a.K; ++p) {
+          for (int p = pos + NHIT; p < a.K; ++p) {
             const int id = sid[p];
             if (id >= n0 + SEG) break;
             zg[sslot[p]] = stage[sr_own * PITCH + (id - n0)];
@@ -216,18 +249,45 @@ __device__ __forceinline__ void logits_tile(const SliceArgs &a, int mt, int seg,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
+  return next_pos;
 }
 
+// Persistent: gridDim.x = 8 g workgroups, g per XCD (workgroup b runs on
+// XCD b % 8).  XCD x owns a contiguous share of the tile order (as
+// xcd_swizzle assigns it), and its workgroup s = b / 8 runs tiles s, s + g,
+// s + 2 g, ... of that share, so the g tiles an XCD runs at once are
+// consecutive in the grouped order.
 __global__ __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fast_logits(SliceArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nmt = (a.C + BM - 1) / BM;
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int n = nmt * a.nseg;
+  const int g = gridDim.x / 8, x = blockIdx.x % 8;
+  const int per = (n + 7) / 8, tall = n % 8 == 0 ? 8 : n % 8;
+  const int lo = x < tall ? x * per : tall * per + (x - tall) * (per - 1);
+  const int hi = lo + (x < tall ? per : per - 1);
+  int L = lo + (int)blockIdx.x / 8;
+  if (L >= hi) return;
   int mt, seg;
-  group_tile(tile, nmt, a.nseg, 4, mt, seg);
-  logits_tile<0>(a, mt, seg, lds);
+  group_tile(L, nmt, a.nseg, 4, mt, seg);
+  int pos = first_pos(a, mt, seg);
+  bool issued = false;
+  for (;;) {
+    const int Ln = L + g;
+    int nmt_, nseg_ = 0;
+    if (Ln < hi)
+      group_tile(Ln, nmt, a.nseg, 4, nmt_, nseg_);
+    else
+      nmt_ = -1;
+    pos = logits_tile<0>(a, mt, seg, lds, issued, pos, nmt_, nseg_);
+    if (Ln >= hi) break;
+    L = Ln;
+    mt = nmt_;
+    seg = nseg_;
+    issued = true;
+  }
 }
 
 // Rows flagged by k_lse_fix: one workgroup per vocabulary segment walks the
@@ -240,7 +300,7 @@ void k_fast_logits_redo(SliceArgs a) {
   const int seg = xcd_swizzle(blockIdx.x, gridDim.x);
   for (int mt = 0; mt < nmt; ++mt) {
     if (a.tile_flags[mt] == 0) continue;
-    logits_tile<1>(a, mt, seg, lds);
+    logits_tile<1>(a, mt, seg, lds, false, -1, -1, 0);
     __syncthreads();
   }
 }
@@ -403,6 +463,20 @@ __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
               a.ldh, a.frow);
 }
 
+// Compute units of the current device (cached per device).
+int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <typename K>
 hipError_t launch(K kern, int grid, const SliceArgs &a, hipStream_t s, int lds, int threads) {
   if (grid <= 0) return hipSuccess;
@@ -444,7 +518,10 @@ int fast_dh_splits(int C, int d, int nseg, int bn) {
 
 hipError_t launch_fast_logits(const SliceArgs &a, hipStream_t s) {
   if (a.d < BK) return hipErrorInvalidValue;  // the main loop needs one k-step
-  return launch(k_fast_logits, ((a.C + BM - 1) / BM) * a.nseg, a, s, w4::Square::LDS, w4::NT);
+  const int tiles = ((a.C + BM - 1) / BM) * a.nseg;
+  // one workgroup per CU (LDS holds one), at most one per tile, 8 | grid
+  const int grid = 8 * std::max(1, std::min(num_cus() / 8, (tiles + 7) / 8));
+  return launch(k_fast_logits, grid, a, s, LG_LDS, w4::NT);
 }
 
 template <class S>
@@ -467,7 +544,7 @@ hipError_t launch_transpose_h(const SliceArgs &a, hipStream_t s) {
 
 hipError_t launch_flagged_rows(const SliceArgs &a, hipStream_t s) {
   if (!a.fast) return hipSuccess;
-  hipError_t e = launch(k_fast_logits_redo, a.nseg, a, s, w4::Square::LDS, w4::NT);
+  hipError_t e = launch(k_fast_logits_redo, a.nseg, a, s, LG_LDS, w4::NT);
   if (e != hipSuccess) return e;
   return launch_fix_flagged(a, s);
 }

@@ -65,6 +65,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_res(const void *base
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations
+// complete, then s_barrier.  Unlike __syncthreads (whose fence waits for
+// every global load in flight), a prefetch into another LDS region keeps
+// going.  The "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Grouped tile order: tiles run in groups of GM consecutive M-tiles, the
 // M index fastest, then N, so the ~32 tiles an XCD runs at once form a
 // GM x (32/GM) block whose operand slices are shared through its L2.
@@ -419,15 +428,20 @@ struct NoHook {
 // The loop body is two k-steps, so each access names its stage statically.
 // `hook` runs once the first k-step's operands, and every load the caller
 // issued before the loop, have landed: loads it issues complete during the
-// first k-step (and are waited for at its end).
+// first k-step (and are waited for at its end).  `issued`: the caller has
+// already issued the first k-step's copies into s0 (all of them, from every
+// wave, with the operands of this call).
 template <class S, class CA, class CB, class F>
 __device__ __forceinline__ void nt_loop_stages(CA &ca, CB &cb, int kbeg, int nk,
                                                char *__restrict__ s0, char *__restrict__ s1,
                                                const FragOff<S> &fo,
-                                               f32x4 (&acc)[S::TMB][S::TNB], F &hook) {
+                                               f32x4 (&acc)[S::TMB][S::TNB], F &hook,
+                                               bool issued) {
   u32x4 fa0[S::TMB], fb0[S::TNB], fa1[S::TMB], fb1[S::TNB];
-  ca.issue_all(s0, kbeg);
-  cb.issue_all(s0 + S::OPA, kbeg);
+  if (!issued) {
+    ca.issue_all(s0, kbeg);
+    cb.issue_all(s0 + S::OPA, kbeg);
+  }
   wait_vm0();
   __syncthreads();
   hook();
@@ -462,18 +476,18 @@ __device__ __forceinline__ void nt_loop_stages(CA &ca, CB &cb, int kbeg, int nk,
 
 // Main loop: acc = A[m0.., kbeg + 64 nk) B[n0.., ...)^T, operands copied by
 // DMA (K- or MN-contiguous as S says); nk >= 1.  On return every copy has
-// landed; callers reusing LDS call __syncthreads first.  `hook`: see
-// nt_loop_stages.
+// landed; callers reusing LDS call __syncthreads first.  `hook` and
+// `issued`: see nt_loop_stages (the first stage is at lds).
 template <class S, class CA, class CB, class F = NoHook>
 __device__ __forceinline__ void nt_loop(CA &ca, CB &cb, int kbeg, int nk, char *lds, int wm,
                                         int wn, int lane, f32x4 (&acc)[S::TMB][S::TNB],
-                                        F hook = F()) {
+                                        F hook = F(), bool issued = false) {
   const FragOff<S> fo(wm, wn, lane);
   // the second stage's offset is hidden from the compiler: with both stages
   // at constant offsets of one array it drops the restrict information
   int st = S::STB;
   asm volatile("" : "+s"(st));
-  nt_loop_stages<S>(ca, cb, kbeg, nk, lds, lds + st, fo, acc, hook);
+  nt_loop_stages<S>(ca, cb, kbeg, nk, lds, lds + st, fo, acc, hook, issued);
 }
 
 // Wait states between the last MFMA and the first read of its accumulator
