@@ -478,7 +478,7 @@ hipError_t launch_div(const DivArgs &a, hipStream_t s) {
     const int shift = ps * RADIX_BITS;
     hipLaunchKernelGGL(k_radix_hist, dim3(nblk), dim3(256), 0, s, a.keys[cur], n, shift, a.hist,
                        nblk);
-    scan_excl(a.hist, (int64_t)RADIX * nblk, a.bsum, s);
+    if (hipError_t e = scan_excl(a.hist, (int64_t)RADIX * nblk, a.bsum, s)) return e;
     hipLaunchKernelGGL(k_radix_scatter, dim3(nblk), dim3(256), 0, s, a.keys[cur], a.vals[cur],
                        a.keys[cur ^ 1], a.vals[cur ^ 1], n, shift, a.hist, nblk);
     cur ^= 1;
@@ -486,8 +486,8 @@ hipError_t launch_div(const DivArgs &a, hipStream_t s) {
   const int gv = (a.V + 1 + 255) / 256;
   hipLaunchKernelGGL(k_div_segments, dim3(gv), dim3(256), 0, s, a, a.keys[cur]);
   hipLaunchKernelGGL(k_div_units, dim3(gv), dim3(256), 0, s, a);
-  scan_excl(a.unit_start, (int64_t)a.V + 1, a.bsum, s);
-  scan_excl(a.part_start, (int64_t)a.V + 1, a.bsum, s);
+  if (hipError_t e = scan_excl(a.unit_start, (int64_t)a.V + 1, a.bsum, s)) return e;
+  if (hipError_t e = scan_excl(a.part_start, (int64_t)a.V + 1, a.bsum, s)) return e;
   const int64_t max_units = n / DIV_UNIT + a.V;
   const int gw = (int)((max_units + ROWS - 1) / ROWS);
   if (bf16)
