@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kd_device.h"
 #include "kd_internal.h"
@@ -466,18 +467,19 @@ __global__ __launch_bounds__(256) void k_transpose_h(SliceArgs a) {
               a.ldh, a.frow);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that
+// race on the first query store the same value).
 int num_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <typename K>
