@@ -222,10 +222,10 @@ def main():
     ap.add_argument("--workload", default="t32k")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--sweep", default="1024,2048,4096,8192",
+    ap.add_argument("--sweep", default="1024,2048,4096,8192,16384,32768",
                     help="slice sizes timed after the main measurement (loss "
-                         "op; a few steps each, reported as chunk_sweep); "
-                         "empty to skip")
+                         "op; a few steps each, reported as chunk_sweep, with "
+                         "the workspace each needs); empty to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc "
