@@ -47,8 +47,11 @@ using namespace tile;
 // passes of 64 consecutive tile rows staged by all four waves: pass p stages
 // blocks 2p and 2p + 1 of both wave rows, and stage row sr is tile row
 // 64 p + sr.  Thread (pr, part) = (tid / 8, tid % 8) takes the two rows
-// 2 pr and 2 pr + 1 and the 8-column groups part, part + 8, ... of them, so
-// the 8 threads of a row store whole 128-byte lines of P~.
+// pr and pr + 32 and the 8-column groups part, part + 8, ... of them, so
+// the 8 threads of a row store whole 128-byte lines of P~.  With the stage
+// pitch of 260 floats, the 16-byte reads of 16 lanes (two rows, one pitch
+// apart) and the 4-byte staging writes of 64 lanes (four rows 4 apart) both
+// fall in distinct LDS banks.
 //
 // The epilogue stages in the LDS above the main loop's first stage, so a
 // workgroup that runs several tiles issues the next tile's first k-step
@@ -129,7 +132,7 @@ __device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, 
   for (int pass = 0; pass < 4; ++pass)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int r = m0 + 64 * pass + 2 * pr + q;
+      const int r = m0 + 64 * pass + pr + 32 * q;
       sh[pass][q] = INFINITY;
       if (grads && r < a.C && (MODE == 0 || a.flag[r])) sh[pass][q] = a.shift[r];
     }
@@ -173,7 +176,7 @@ __device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, 
     }
     // Rows one at a time (fewer live registers): z of the row, the
     // statistics, and P~ packed to bf16 pairs of adjacent columns.
-    const int r0 = m0 + 64 * pass + 2 * pr;
+    const int r0 = m0 + 64 * pass + pr;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float v[CPT];
@@ -182,7 +185,7 @@ __device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int col = j * 8 * TPR + part * 8 + 4 * h;
-          const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + (2 * pr + q) * PITCH + col);
+          const f32x4 z = *reinterpret_cast<const f32x4 *>(stage + (pr + 32 * q) * PITCH + col);
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[j * 8 + 4 * h + u] = z[u];
         }
@@ -205,9 +208,9 @@ __device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, 
           v[c] = pv * cq;
         }
         const float sum = group8_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
-        if (part == 0 && r0 + q < a.C) {
-          a.mseg[(size_t)(r0 + q) * a.nseg + seg] = mx;
-          a.sseg[(size_t)(r0 + q) * a.nseg + seg] = sum;
+        if (part == 0 && r0 + 32 * q < a.C) {
+          a.mseg[(size_t)(r0 + 32 * q) * a.nseg + seg] = mx;
+          a.sseg[(size_t)(r0 + 32 * q) * a.nseg + seg] = sum;
         }
       } else {
 #pragma unroll
@@ -215,7 +218,7 @@ __device__ __forceinline__ int logits_tile(const SliceArgs &a, int mt, int seg, 
       }
       // rows past C (and, in MODE 1, rows not flagged: +inf shift) are not
       // stored
-      const int r = r0 + q;
+      const int r = r0 + 32 * q;
       if (grads && r < a.C && (MODE == 0 || sh[pass][q] != INFINITY)) {
         uint16_t *dst = P + (size_t)r * a.ldp + n0 + part * 8;
 #pragma unroll
