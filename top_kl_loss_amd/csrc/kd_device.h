@@ -96,6 +96,29 @@ __device__ __forceinline__ float group8_sum(float v) {
   return v + dpp_mov<0x141>(v);
 }
 
+// Integer forms: the sum over each group of 8 lanes (in all 8), and the
+// inclusive prefix sum over it (g = the lane's index in its group; DPP
+// row shifts by 1, 2, 4 with out-of-row sources read as 0, and a lane adds
+// only what comes from its own group).
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int group8_sum_i(int v) {
+  v += dpp_mov_i<0xB1>(v);
+  v += dpp_mov_i<0x4E>(v);
+  return v + dpp_mov_i<0x141>(v);
+}
+__device__ __forceinline__ int group8_scan_i(int v, int g) {
+  int y = dpp_mov_i<0x111>(v);  // row_shr:1
+  if (g >= 1) v += y;
+  y = dpp_mov_i<0x112>(v);      // row_shr:2
+  if (g >= 2) v += y;
+  y = dpp_mov_i<0x114>(v);      // row_shr:4
+  if (g >= 4) v += y;
+  return v;
+}
+
 // Wave-wide (64-lane) reductions through cross-lane shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -118,19 +118,31 @@ void k_tk_gemm(TkArgs a) {
                 w4::acc_col4(j, lane)] = acc[2 * pass + ii][j][e];
     __syncthreads();
     const int cb0 = part * CPT;
+    if (MODE == SAMPLE) {
 #pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-      const int sr = tid / TPR + q * (w4::NT / TPR);
-      const int r = row_of(pass, q);
-      const float *srow = stage + sr * PITCH + cb0;
-      if (MODE == SAMPLE) {
+      for (int q = 0; q < RPT; ++q) {
+        const int sr = tid / TPR + q * (w4::NT / TPR);
+        const int r = row_of(pass, q);
+        const float *srow = stage + sr * PITCH + cb0;
         if (r < a.C) {
           float *dst = a.zs + (size_t)r * a.ldzs + nt * SEG + cb0;
 #pragma unroll
           for (int c = 0; c < CPT; c += 4)
             *reinterpret_cast<f32x4 *>(dst + c) = *reinterpret_cast<const f32x4 *>(srow + c);
         }
-      } else {
+      }
+    } else {
+      // The thread's two rows in three phases, so that their candidate
+      // counters take one atomic round trip together: (1) which of its 32
+      // columns pass the row's threshold, their count and its exclusive
+      // prefix over the row's 8 threads; (2) one atomic add per row by the
+      // row's last thread, reserving the row's slots; (3) the candidates.
+      uint32_t mq[RPT];
+      int exq[RPT], totq[RPT], bq[RPT];
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int sr = tid / TPR + q * (w4::NT / TPR);
+        const float *srow = stage + sr * PITCH + cb0;
         const float tv = th_v[q];
         const int ti = th_i[q];
         uint32_t m = 0u;
@@ -147,18 +159,25 @@ void k_tk_gemm(TkArgs a) {
         const int lim = a.V - (n0 + cb0);  // columns of this thread below V
         if (lim < CPT) m = lim <= 0 ? 0u : (m & ((1u << lim) - 1u));
         const int n = __popc(m);
-        int incl = n;
+        mq[q] = m;
+        exq[q] = group8_scan_i(n, part) - n;
+        totq[q] = group8_sum_i(n);
+      }
 #pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) {
-          const int y = __shfl_up(incl, o, TPR);
-          if (part >= o) incl += y;
-        }
-        const int total = __shfl(incl, TPR - 1, TPR);
-        int base = 0;
-        if (part == TPR - 1 && total > 0 && r < a.C) base = atomicAdd(a.cnt + r, total);
-        base = __shfl(base, TPR - 1, TPR);
+      for (int q = 0; q < RPT; ++q) {
+        const int r = row_of(pass, q);
+        bq[q] = 0;
+        if (part == TPR - 1 && totq[q] > 0 && r < a.C) bq[q] = atomicAdd(a.cnt + r, totq[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int sr = tid / TPR + q * (w4::NT / TPR);
+        const int r = row_of(pass, q);
+        const float *srow = stage + sr * PITCH + cb0;
+        const int base = group8_sum_i(bq[q]);  // (only the last thread's is nonzero)
+        uint32_t m = mq[q];
         if (m != 0u && r < a.C) {
-          int pos = base + incl - n;
+          int pos = base + exq[q];
           uint64_t *dst = a.cand + (size_t)r * a.cap;
           while (m != 0u) {
             const int i = __builtin_ctz(m);
@@ -167,7 +186,7 @@ void k_tk_gemm(TkArgs a) {
             ++pos;
           }
         }
-        if (part == TPR - 1 && r < a.C && total > 0 && base + total > a.cap) a.ovf[r] = 1;
+        if (part == TPR - 1 && r < a.C && totq[q] > 0 && base + totq[q] > a.cap) a.ovf[r] = 1;
       }
     }
     __syncthreads();
