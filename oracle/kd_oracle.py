@@ -169,7 +169,8 @@ def kd_topk_kl(H, W, topk_idx, topk_logit, mask, tau, chunk=None):
     }
 
 
-def slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
+def slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid,
+                want_dw=True):
     """One slice of the chunked loss (the body of ``kd_topk_kl``'s loop).
 
     For the token rows given, with the whole batch's valid-token count
@@ -177,9 +178,10 @@ def slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
     log-softmax over the vocabulary, the forward KL against the teacher's
     top-K distribution, and the logit gradient G = tau/N mask (p - q_scat)
     with its two products.  Returns (row_loss = mask*KL [R], lse [R] of z/tau,
-    dH rows G W [R, d], the slice's dW contribution G^T H_rows [V, d]), all
-    fp64.  Slices of a batch are independent given n_valid, so a full-size
-    batch can be evaluated slice by slice with the results summed.
+    dH rows G W [R, d], the slice's dW contribution G^T H_rows [V, d], or
+    None when ``want_dw`` is false), all fp64.  Slices of a batch are
+    independent given n_valid, so a full-size batch can be evaluated slice by
+    slice with the results summed.
     """
     H_rows = _f64(H_rows)
     W = _f64(W)
@@ -198,7 +200,7 @@ def slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
     # dL/dz = tau/N * mask * (p - q_scat)
     G = np.exp(log_p) - scattered_teacher(ids, q, V)
     G *= (grad_scale * m)[:, None]
-    return m * kl, lse, G @ W, G.T @ H_rows
+    return m * kl, lse, G @ W, (G.T @ H_rows if want_dw else None)
 
 
 def row_lse(H_rows, W, tau, rows_per_block=256):
@@ -225,7 +227,7 @@ def rows_loss_and_dh(H_rows, W, idx_rows, logit_rows, mask_rows, tau, n_valid):
     checked one by one.  Returns (row_loss [R] = mask*KL, dH [R,d]).
     """
     rl, _, dH_rows, _ = slice_terms(H_rows, W, idx_rows, logit_rows, mask_rows,
-                                    tau, n_valid)
+                                    tau, n_valid, want_dw=False)
     return rl, dH_rows
 
 
