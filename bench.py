@@ -631,8 +631,10 @@ def bench_teacher(args):
 
     # algorithmic work of the dominant kernel per launch
     nseg = (V + 255) // 256
-    ns = min(32, nseg)
-    stride = 1 if nseg <= 32 else nseg // 32
+    # the library's sampled-segment count: about K nseg / ns <= 4096
+    # candidates expected per row, ns in [32, 128], at most nseg
+    ns = min(max(-(-K * nseg // 4096), 32), 128, nseg)
+    stride = 1 if ns == nseg else nseg // ns
     cols = {11: ns * 256, 13: (nseg - ns) * 256}.get(dom)
     if cols is not None:
         flops_launch = 2.0 * chunk * d * cols

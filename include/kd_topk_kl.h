@@ -349,9 +349,10 @@ int kd_topk_div_fwd_bwd(int32_t kind, const void *H, const void *W,
 /*
  * kd_teacher_topk_workspace_size -- bytes of scratch device memory needed by
  * kd_teacher_topk for these sizes (per slice of `chunk` rows: the logits of
- * 32 sampled vocabulary segments, 8192 candidate slots of 8 bytes and four
- * words per row; bf16 with d % 64 == 0 only, otherwise 256 bytes).  It grows
- * with chunk, never with T*V.  Arguments and return values as for
+ * ns sampled vocabulary segments of 256 ids, ns = 32, or more when K *
+ * ceil(V / 256) > 131072, up to 128; 8192 candidate slots of 8 bytes and
+ * four words per row; bf16 with d % 64 == 0 only, otherwise 256 bytes).  It
+ * grows with chunk, never with T*V.  Arguments and return values as for
  * kd_teacher_topk; `bytes_out` is a host pointer.
  */
 int kd_teacher_topk_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,

@@ -64,6 +64,17 @@ def assert_grad_close(g, o, dtype, what):
         assert c >= tol["cos"], f"{what}: cosine {c:.6f} < {tol['cos']}"
 
 
+def assert_rows_kl(g, o, where):
+    """Every row's KL within 1e-3 of its own value (padding rows exactly 0)."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    pad = o == 0.0
+    assert np.all(g[pad] == 0.0), f"{where}: padding rows carry a loss"
+    rel = np.abs(g[~pad] - o[~pad]) / np.abs(o[~pad])
+    assert rel.size == 0 or rel.max() <= 1e-3, \
+        f"{where}: row KL rel {rel.max():.2e} at row {int(np.argmax(rel))}"
+
+
 def assert_loss_close(g, o, dtype):
     tol = TOL[dtype]["loss"]
     rel = abs(g - o) / max(abs(o), 1e-30)

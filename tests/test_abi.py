@@ -135,6 +135,26 @@ def test_teacher_workspace_is_bounded_by_the_slice():
     assert kd.kd_teacher_topk_workspace_size(64, 72, 5000, 100, 64, kd.KD_BF16) == 256
 
 
+def test_teacher_samples_grow_with_k_and_vocabulary():
+    """The sampled segments per row: 32, or ceil(K nseg / 4096) when larger
+    (so that a row expects at most about half of its 8192 candidate slots),
+    at most 128; the workspace holds 1 KiB of sampled logits per segment."""
+    C = 256
+    fixed = 8192 * 8 + 16
+
+    def samples(V, K):
+        ws = kd.kd_teacher_topk_workspace_size(C, 2880, V, K, C, kd.KD_BF16)
+        ns, rest = divmod(ws - C * fixed, C * 256 * 4)
+        assert 0 <= rest < 4096, (V, K, ws)
+        return ns
+
+    assert samples(201088, 100) == 32            # K nseg = 78600
+    assert samples(201088, 256) == 50            # ceil(256 * 786 / 4096)
+    assert samples(745654, 100) == 72            # V d just below 2^31 at d = 2880
+    assert samples(745654, 256) == 128           # capped
+    assert samples(5000, 100) == 20              # fewer segments than 32: all
+
+
 @pytest.mark.parametrize("args,code", [
     ((0, 512, 8192, 100, 64, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),
     ((256, 512, 99, 100, 64, kd.KD_BF16), kd.KD_ERR_INVALID_ARG),

@@ -87,7 +87,7 @@ class FullRun:
             self.lse[s0:s1] = lse
             for c, o in self.out.items():
                 where = f"{x.name} chunk {c} rows {s0}:{s1}"
-                _check_rows_kl(o["rl"][s0:s1], rl, where)
+                G.assert_rows_kl(o["rl"][s0:s1], rl, where)
                 G.assert_grad_close(o["dH"][s0:s1], dH, x.dtype, f"{where} dH")
         self.rows_done += r1 - r0
         _say(f"{x.name}: oracle rows {r0}:{r1} compared")
@@ -109,16 +109,6 @@ class FullRun:
             assert np.array_equal(self.fwd["rl"], self.out[c]["rl"])
             err = np.abs(self.fwd["lse"] - self.lse).max() / np.abs(self.lse).max()
             assert err <= 1e-5, f"lse max rel {err:.2e}"
-
-
-def _check_rows_kl(g, o, where):
-    """Every row's KL within 1e-3 of its own value (padding rows exactly 0)."""
-    g = np.asarray(g, np.float64)
-    pad = o == 0.0
-    assert np.all(g[pad] == 0.0), f"{where}: padding rows carry a loss"
-    rel = np.abs(g[~pad] - o[~pad]) / np.abs(o[~pad])
-    assert rel.size == 0 or rel.max() <= 1e-3, \
-        f"{where}: row KL rel {rel.max():.2e} at row {int(np.argmax(rel))}"
 
 
 _RUNS = {}

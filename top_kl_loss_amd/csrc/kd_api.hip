@@ -154,17 +154,23 @@ struct TkLayout {
   size_t o_zs, o_thv, o_thi, o_cnt, o_ovf, o_cand, total;
 };
 
-TkLayout make_tk_layout(int64_t T, int64_t d, int64_t V, int32_t chunk, kd_dtype dtype) {
+TkLayout make_tk_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
+                        kd_dtype dtype) {
   TkLayout L{};
   L.C = (int)(chunk < T ? chunk : T);
   L.nseg = (int)((V + kd::SEG - 1) / kd::SEG);
   L.fast = kd::use_fast(dtype == KD_BF16, L.C, d, V, (int64_t)L.nseg * kd::SEG);
-  if (L.nseg <= kd::TK_NSAMPLE) {
+  // sampled segments: enough that about K nseg / ns <= TK_CAP / 2 candidates
+  // are expected per row, within [TK_NSAMPLE, TK_NSAMPLE_MAX]
+  const int64_t want = ((int64_t)K * L.nseg + kd::TK_CAP / 2 - 1) / (kd::TK_CAP / 2);
+  const int ns = (int)std::min<int64_t>(std::max<int64_t>(want, kd::TK_NSAMPLE),
+                                        kd::TK_NSAMPLE_MAX);
+  if (L.nseg <= ns) {
     L.ns = L.nseg;
     L.sstride = 1;
   } else {
-    L.ns = kd::TK_NSAMPLE;
-    L.sstride = L.nseg / kd::TK_NSAMPLE;
+    L.ns = ns;
+    L.sstride = L.nseg / ns;
   }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -442,7 +448,7 @@ int kd_teacher_topk_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
   if (!bytes_out) return KD_ERR_INVALID_ARG;
   const int st = check_tk_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
-  *bytes_out = make_tk_layout(T, d, V, chunk, dtype).total;
+  *bytes_out = make_tk_layout(T, d, V, K, chunk, dtype).total;
   return KD_OK;
 }
 
@@ -454,7 +460,7 @@ int kd_teacher_topk(const void *H, const void *W, kd_dtype dtype, int64_t T,
     return KD_ERR_INVALID_ARG;
   const int st = check_tk_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
-  const TkLayout L = make_tk_layout(T, d, V, chunk, dtype);
+  const TkLayout L = make_tk_layout(T, d, V, K, chunk, dtype);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return KD_ERR_WORKSPACE;

@@ -132,7 +132,11 @@ hipError_t launch_gemm_dw(const SliceArgs &a, bool bf16, hipStream_t s);
 
 // Sampled vocabulary segments per row (evenly spaced, segment 0 included);
 // the K-th best entry among them bounds the row's K-th best from below.
+// At least TK_NSAMPLE; more for large K nseg, so that a row without
+// structure expects about K nseg / ns <= TK_CAP / 2 candidates; at most
+// TK_NSAMPLE_MAX (the threshold kernel holds the samples of a row in LDS).
 constexpr int TK_NSAMPLE = 32;
+constexpr int TK_NSAMPLE_MAX = 128;
 // Candidate slots per row; a row with more candidates than this is
 // recomputed by the row-streaming kernel.
 constexpr int TK_CAP = 8192;

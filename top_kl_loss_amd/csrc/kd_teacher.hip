@@ -13,8 +13,10 @@
 // smallest keys.
 //
 // Tuned path (bf16, d % 64 == 0), per slice of C rows:
-//  1. k_tk_gemm<SAMPLE>: logits of TK_NSAMPLE evenly spaced vocabulary
-//     segments (segment 0 included), written to a small [C, ns*256] buffer.
+//  1. k_tk_gemm<SAMPLE>: logits of ns evenly spaced vocabulary segments
+//     (segment 0 included; ns = 32, or more for large K nseg so that about
+//     K nseg / ns <= TK_CAP / 2 candidates are expected per row), written to
+//     a small [C, ns*256] buffer.
 //  2. k_tk_theta: per row, the K-th smallest key among the sampled entries
 //     (radix select).  The K sampled entries are real entries of the row, so
 //     the row's K-th smallest key is no larger: every top-K entry has a key
@@ -197,7 +199,7 @@ void k_tk_gemm(TkArgs a) {
 // One workgroup per row: the K-th smallest key among the sampled entries,
 // and those K entries as the row's first candidates.
 __global__ __launch_bounds__(256) void k_tk_theta(TkArgs a) {
-  __shared__ uint32_t hi[TK_NSAMPLE * SEG];
+  extern __shared__ uint32_t hi[];  // ns * SEG
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sc[8];
   __shared__ uint64_t res;
@@ -207,23 +209,25 @@ __global__ __launch_bounds__(256) void k_tk_theta(TkArgs a) {
   const int sstride = a.sstride;
   const float *src = a.zs + (size_t)r * a.ldzs;
   auto id_of = [sstride](int i) { return (i / SEG) * sstride * SEG + (i % SEG); };
-  // n is a multiple of 256 (ns segments): 16-byte loads, all of a thread's
+  // n is a multiple of 256 (ns segments): 16-byte loads, U of a thread's
   // loads in flight before their use
-  constexpr int U = TK_NSAMPLE * SEG / 1024;
-  f32x4 zv[U];
+  constexpr int U = 8;
+  for (int base = 0; base < n; base += U * 1024) {
+    f32x4 zv[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = (u * 256 + tid) * 4;
-    if (i < n) zv[u] = *reinterpret_cast<const f32x4 *>(src + i);
-  }
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (u * 256 + tid) * 4;
+      if (i < n) zv[u] = *reinterpret_cast<const f32x4 *>(src + i);
+    }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = (u * 256 + tid) * 4;
-    if (i < n) {
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (u * 256 + tid) * 4;
+      if (i < n) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // entries past the vocabulary rank after every real entry
-        hi[i + c] = id_of(i + c) < a.V ? key_hi(zv[u][c]) : 0xffffffffu;
+        for (int c = 0; c < 4; ++c) {
+          // entries past the vocabulary rank after every real entry
+          hi[i + c] = id_of(i + c) < a.V ? key_hi(zv[u][c]) : 0xffffffffu;
+        }
       }
     }
   }
@@ -363,9 +367,8 @@ hipError_t launch_tk_sample(const TkArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_tk_theta(const TkArgs &a, hipStream_t s) {
-  if (a.C <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tk_theta, dim3(a.C), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.ns < 1 || a.ns > TK_NSAMPLE_MAX) return hipErrorInvalidValue;
+  return launch_dyn(k_tk_theta, a.C, 256, a.ns * SEG * (int)sizeof(uint32_t), a, s);
 }
 
 hipError_t launch_tk_filter(const TkArgs &a, hipStream_t s) {
