@@ -215,7 +215,7 @@ def main():
                          "kd_topk_kl_fwd (loss only); bwd: kd_topk_kl_bwd "
                          "(gradients, logits recomputed); teacher_topk: "
                          "kd_teacher_topk, the teacher cache build; "
-                         "entropy_filter: kd_entropy_filter (top 70% of "
+                         "entropy_filter: kd_entropy_filter (top 70%% of "
                          "tokens by teacher entropy); reverse_kl / jsd: "
                          "kd_topk_div_fwd_bwd, the divergence over the "
                          "top-K support")
