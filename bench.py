@@ -203,6 +203,50 @@ def config_key(args):
     return f"{args.op} {args.workload} chunk {args.chunk or default}"
 
 
+def bench_vendor_gemm(args):
+    """Reference timing, outside the library: torch's bf16 matrix products
+    (hipBLASLt on ROCm) on the three products of one slice of the workload,
+    C = the slice size, with the operands in the layouts the loss's kernels
+    read (H_c [C, d] and W [V, d] row-major, probabilities [C, V] row-major)
+    and bf16 outputs, no epilogue.  Context for the loss's GEMM rates on the
+    same chip and clock, not a result of the library."""
+    import torch
+
+    import synth
+    spec = synth.WORKLOADS[args.workload]
+    C, d, V = args.chunk or spec["chunk"], spec["d"], spec["V"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    H = torch.randn(C, d, device=dev, generator=g).to(torch.bfloat16)
+    W = (torch.randn(V, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    P = torch.rand(C, V, device=dev, generator=g).to(torch.bfloat16)
+    flop = 2.0 * C * d * V
+    products = (("logits", "H_c W^T -> [C, V]", lambda: torch.nn.functional.linear(H, W)),
+                ("dH", "P W -> [C, d]", lambda: torch.mm(P, W)),
+                ("dW", "P^T H_c -> [V, d]", lambda: torch.mm(P.t(), H)))
+    out = {}
+    for name, what, f in products:
+        for _ in range(max(args.warmup, 1)):
+            f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        ms = ts[len(ts) // 2]
+        out[name] = {"product": what, "ms_median": round(ms, 4), "ms_min": round(ts[0], 4),
+                     "tflops": round(flop / ms / 1e9, 2),
+                     "frac_of_bf16_peak": round(flop / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        log(f"vendor {name}: {ms:.3f} ms, {flop / ms / 1e9:.1f} TFLOP/s")
+    print(json.dumps({"reference": "vendor bf16 GEMM (torch.mm -> hipBLASLt), no epilogue",
+                      "workload": args.workload, "C": C, "d": d, "V": V,
+                      "flops_per_product": flop, "steps": args.steps, "products": out}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +276,11 @@ def main():
                          "runs (FETCH_SIZE, WRITE_SIZE; csv output) of this "
                          "--op/--workload/--chunk made with --copy-calibration "
                          "BYTES, then exit (no GPU needed)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="reference only, not the loss: time the vendor "
+                         "library's plain bf16 GEMMs (torch.mm -> hipBLASLt) "
+                         "on the three products of one slice of --workload "
+                         "(no epilogue), print one JSON line and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed region, copy BYTES device-to-device "
                          "3 times (a reference kernel of known traffic for "
@@ -249,6 +298,8 @@ def main():
             raise SystemExit("--record-traffic needs --copy-calibration BYTES")
         return record_traffic(args.op, config_key(args), *args.record_traffic,
                               args.copy_calibration)
+    if args.vendor_gemm:
+        return bench_vendor_gemm(args)
     if args.op == "teacher_topk":
         return bench_teacher(args)
     if args.op == "entropy_filter":
@@ -402,7 +453,11 @@ def main():
     flops_step = (2.0 if args.op == "fwd" else 6.0) * T * d * V
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     tokens_s = T * args.steps / wall
-    flops_launch = 2.0 * chunk * d * V if dom in GEMM_KERNELS else None
+    # Each of the three GEMMs does 2 T d V flops per step in all; per launch
+    # that is the step's share per launch of the kernel (the dW GEMM runs
+    # once per group of slices, and a ragged last slice is smaller).
+    dom_per_step = len(dom_ms) / args.steps
+    flops_launch = 2.0 * T * d * V / dom_per_step if dom in GEMM_KERNELS else None
     if flops_launch is not None:
         ach = flops_launch / (dom_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kd.KERNEL_NAMES[dom],
