@@ -335,7 +335,11 @@ def main():
     lg = torch.from_numpy(x.topk_logit).to(dev)
     mask = None if x.mask is None else torch.from_numpy(x.mask).to(dev)
     T, d, V, K = x.T, x.d, x.V, x.K
-    ws_bytes = kd.kd_topk_kl_workspace_size(T, d, V, K, chunk, dt_code)
+    # the forward alone has a workspace of its own (no probabilities or
+    # gradient buffers)
+    ws_size = kd.kd_topk_kl_fwd_workspace_size if args.op == "fwd" else \
+        kd.kd_topk_kl_workspace_size
+    ws_bytes = ws_size(T, d, V, K, chunk, dt_code)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     loss = torch.empty(1, **f32)

@@ -82,7 +82,8 @@ enum {
 
 /*
  * kd_topk_kl_workspace_size -- bytes of scratch device memory needed by
- * kd_topk_kl_fwd_bwd, kd_topk_kl_fwd and kd_topk_kl_bwd for these sizes.
+ * kd_topk_kl_fwd_bwd and kd_topk_kl_bwd (and, larger than it needs,
+ * kd_topk_kl_fwd) for these sizes.
  *
  * The workspace holds the per-slice intermediates of the chunked loss
  * ("Making Knowledge Distillation Cheap Enough to Run at Scale", aipuls.nl,
@@ -143,6 +144,18 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kd_topk_kl_fwd_workspace_size -- bytes of scratch device memory needed by
+ * kd_topk_kl_fwd for these sizes: the per-slice row statistics, teacher
+ * softmax, gathered logits and sorted ids, and the row losses (no
+ * probabilities or gradient buffers; 81 MB at T = 32768, V = 201088,
+ * K = 100, chunk 8192, against 4.2 GB for the fused call).  At most
+ * kd_topk_kl_workspace_size for the same sizes.  Arguments, return codes
+ * and checks as for kd_topk_kl_workspace_size.
+ */
+int kd_topk_kl_fwd_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                                  int32_t chunk, kd_dtype dtype, size_t *bytes_out);
+
+/*
  * kd_topk_kl_fwd -- the loss alone (no gradients): the forward half of the
  * loss for evaluation, or for training with kd_topk_kl_bwd when the
  * backward runs later (the student training step of "Making Knowledge
@@ -152,7 +165,8 @@ int kd_topk_kl_fwd_bwd(const void *H, const void *W, kd_dtype dtype,
  *         too), or NULL.
  * loss and row_loss are bitwise those of kd_topk_kl_fwd_bwd.  It runs the
  * logits GEMM and the row reductions only: about a third of the work.  The
- * workspace is sized by kd_topk_kl_workspace_size.
+ * workspace needs at least kd_topk_kl_fwd_workspace_size bytes (a workspace
+ * sized by kd_topk_kl_workspace_size is larger and also does).
  */
 int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
                    const int32_t *topk_idx, const float *topk_logit,

@@ -202,6 +202,33 @@ def test_teacher_topk_rejects_before_any_hip_call(kw, code):
 
 
 # ------------------------------------------ split forward / backward, cast
+def test_forward_workspace_holds_no_probabilities():
+    # the forward alone keeps the slice's row statistics, teacher softmax,
+    # gathered logits and sorted ids (and T row losses), not the C x V
+    # probabilities or any gradient buffer
+    T, d, V, K = 32768, 2880, 201088, 100
+    nseg = (V + 255) // 256
+    for c in (1024, 8192, 32768):
+        fused = kd.kd_topk_kl_workspace_size(T, d, V, K, c, kd.KD_BF16)
+        fwd = kd.kd_topk_kl_fwd_workspace_size(T, d, V, K, c, kd.KD_BF16)
+        per_slice = c * (5 * 4 * K + (2 + 4 + 4) * nseg + 4)   # q lq zg sid sslot, first mseg sseg, lse
+        assert per_slice + 4 * T <= fwd <= per_slice + 4 * T + 16 * 256
+        assert fwd < fused / 40
+    # the size does not depend on the element type (no probabilities)
+    assert (kd.kd_topk_kl_fwd_workspace_size(T, d, V, K, 8192, kd.KD_F32) ==
+            kd.kd_topk_kl_fwd_workspace_size(T, d, V, K, 8192, kd.KD_BF16))
+    with pytest.raises(kd.KdError) as e:
+        kd.kd_topk_kl_fwd_workspace_size(T, 12, V, K, 8192, kd.KD_BF16)
+    assert e.value.status == kd.KD_ERR_UNSUPPORTED
+
+
+def test_forward_accepts_its_own_workspace_size_only():
+    need = kd.kd_topk_kl_fwd_workspace_size(256, 512, 8192, 100, 64, kd.KD_BF16)
+    assert _fwd_call(ws_bytes=need - 1) == kd.KD_ERR_WORKSPACE
+    # (a workspace of `need` bytes passes every check; the call itself
+    # needs a GPU)
+
+
 def _fwd_call(**kw):
     lib = kd.load_library()
     a = dict(H=256, W=256, dtype=kd.KD_BF16, idx=256, logit=256, mask=None, T=256,

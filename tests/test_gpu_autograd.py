@@ -103,6 +103,32 @@ def test_autograd_gradients_match_the_oracle(x, recompute):
     G.assert_grad_close(G.to_np(W.grad.float()), 3.0 * ref["dW"], x.dtype, "W.grad")
 
 
+@pytest.mark.parametrize("x", _cases(), ids=lambda x: x.name)
+def test_loss_without_gradients_runs_the_forward_alone(x):
+    # under torch.no_grad, or with inputs that need no gradient, the loss is
+    # the forward entry point's (bitwise), carries no graph, and the call
+    # allocates no gradient buffer (less than dW's size at its peak)
+    import torch
+    from top_kl_loss_amd.autograd import topk_kl_loss
+    _say(f"no-grad loss: {x.name}")
+    dev = G.to_device(x)
+    want, _, _ = kd.kd_topk_kl_fwd(dev["H"], dev["W"], dev["topk_idx"],
+                                   dev["topk_logit"], dev["mask"], x.tau, x.chunk)
+    H = dev["H"].clone().requires_grad_(True)
+    W = dev["W"].clone().requires_grad_(True)
+    torch.cuda.synchronize()
+    for ctx, h, w in ((torch.no_grad(), H, W), (torch.enable_grad(), dev["H"], dev["W"])):
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        with ctx:
+            loss = topk_kl_loss(h, w, dev["topk_idx"], dev["topk_logit"], dev["mask"],
+                                x.tau, x.chunk)
+        torch.cuda.synchronize()
+        assert loss.dim() == 0 and not loss.requires_grad and loss.grad_fn is None
+        assert torch.equal(loss.reshape(1), want)
+        assert torch.cuda.max_memory_allocated() - base < x.V * x.d * 4
+
+
 def test_autograd_through_a_student_head_and_a_training_step():
     # H = X A (a projection in front of the loss): the gradient reaches A by
     # the chain rule, and a few SGD steps on (A, W) lower the loss.

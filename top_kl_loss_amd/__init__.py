@@ -21,6 +21,7 @@ __all__ = [
     "KD_F32", "KD_BF16", "KD_FLAG_ACCUMULATE_DW", "KD_MAX_K", "LIB_PATH",
     "KdError", "load_library", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd", "kd_status_string", "kd_set_launch_log",
+    "kd_topk_kl_fwd_workspace_size",
     "EXPORTED_SYMBOLS", "KERNEL_NAMES", "KD_TOPK_MAX_K", "KD_TOPK_MAX_D",
     "kd_teacher_topk_workspace_size", "kd_teacher_topk", "kd_topk_kl_fwd",
     "kd_topk_kl_bwd", "kd_grad_cast", "kd_entropy_filter",
@@ -48,7 +49,7 @@ EXPORTED_SYMBOLS = ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd",
                     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_grad_cast",
                     "kd_entropy_filter_workspace_size", "kd_entropy_filter",
                     "kd_topk_kl_fwd_noalloc", "kd_topk_div_workspace_size",
-                    "kd_topk_div_fwd_bwd")
+                    "kd_topk_div_fwd_bwd", "kd_topk_kl_fwd_workspace_size")
 KD_FILTER_ENTROPY_ABOVE, KD_FILTER_TOP_ENTROPY_FRACTION = 0, 1
 # Kernel ids of the launch log (KD_KERNEL_* in the header).
 KERNEL_NAMES = ("valid_count", "prep_rows", "gemm_logits", "lse_fix",
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH):
         c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_int,
         c.POINTER(c.c_size_t)]
     lib.kd_topk_kl_workspace_size.restype = c.c_int
+    lib.kd_topk_kl_fwd_workspace_size.argtypes = [
+        c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_int32, c.c_int,
+        c.POINTER(c.c_size_t)]
+    lib.kd_topk_kl_fwd_workspace_size.restype = c.c_int
     lib.kd_topk_kl_fwd_bwd.argtypes = [
         c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
         c.c_int64, c.c_int64, c.c_int64, c.c_int32, c.c_float, c.c_int32,
@@ -174,6 +179,15 @@ def kd_topk_kl_workspace_size(T, d, V, K, chunk, dtype) -> int:
     """Workspace bytes for kd_topk_kl_fwd_bwd (see the C header)."""
     out = ctypes.c_size_t(0)
     _check(load_library().kd_topk_kl_workspace_size(
+        int(T), int(d), int(V), int(K), int(chunk), int(dtype),
+        ctypes.byref(out)))
+    return out.value
+
+
+def kd_topk_kl_fwd_workspace_size(T, d, V, K, chunk, dtype) -> int:
+    """Workspace bytes for kd_topk_kl_fwd (see the C header)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_topk_kl_fwd_workspace_size(
         int(T), int(d), int(V), int(K), int(chunk), int(dtype),
         ctypes.byref(out)))
     return out.value
@@ -273,9 +287,9 @@ def _mask_u8(mask):
     return mask.to(torch.uint8)
 
 
-def _workspace(T, d, V, K, chunk, dt, workspace, dev):
+def _workspace(T, d, V, K, chunk, dt, workspace, dev, size=None):
     import torch
-    ws_bytes = kd_topk_kl_workspace_size(T, d, V, K, chunk, dt)
+    ws_bytes = (size or kd_topk_kl_workspace_size)(T, d, V, K, chunk, dt)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     elif workspace.numel() < ws_bytes:
@@ -344,7 +358,8 @@ def kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask=None, tau=1.0,
     dev = H.device
     with _Call(dev, stream, sync) as call:
         mask = _mask_u8(mask)
-        workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev)
+        workspace = _workspace(T, d, V, K, chunk, dt, workspace, dev,
+                               size=kd_topk_kl_fwd_workspace_size)
         f32 = dict(dtype=torch.float32, device=dev)
         loss = torch.empty(1, **f32)
         rl = torch.empty(T, **f32) if row_loss else None

@@ -97,11 +97,21 @@ def topk_kl_loss(H, W, topk_idx, topk_logit, mask=None, tau=1.0, chunk=None,
 
     divergence: "forward_kl" (the above), or "reverse_kl" / "jsd": the
     divergence between the student restricted to the K cached ids
-    (renormalised) and the teacher there (kd_topk_div_fwd_bwd; no chunk)."""
+    (renormalised) and the teacher there (kd_topk_div_fwd_bwd; no chunk).
+
+    When no gradient is wanted (grad mode off, or neither H nor W requires
+    one) the forward KL runs kd_topk_kl_fwd alone."""
     if entropy_filter is not None:
         mode, param = entropy_filter
         mask, _ = kd_entropy_filter(topk_logit, mask, tau, mode, param,
                                     entropy=False)
+    if divergence == "forward_kl" and not (
+            torch.is_grad_enabled() and (H.requires_grad or W.requires_grad)):
+        # no gradient wanted (evaluation, torch.no_grad): the forward alone,
+        # a third of the work and no gradient buffers; the same loss bits
+        loss, _, _ = kd_topk_kl_fwd(H, W, topk_idx, topk_logit, mask, tau,
+                                    chunk, row_loss=False, lse=False)
+        return loss.reshape(())
     return TopKKLLossFunction.apply(H, W, topk_idx, topk_logit, mask, tau,
                                     chunk, recompute, divergence)
 

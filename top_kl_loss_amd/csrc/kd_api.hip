@@ -80,7 +80,8 @@ int check_sizes(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
 
 // fwd_only: the regions the forward alone touches (no probabilities, G,
 // gradient factors, dH partials or the transposed hidden states): the
-// compact layout of the allocation-free forward entry point.
+// compact layout of the forward entry points (kd_topk_kl_fwd and the
+// allocation-free kd_topk_kl_fwd_noalloc).
 Layout make_layout(int64_t T, int64_t d, int64_t V, int32_t K, int32_t chunk,
                    kd_dtype dtype, bool fwd_only = false) {
   Layout L{};
@@ -204,6 +205,15 @@ int kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
   const int st = check_sizes(T, d, V, K, chunk, dtype);
   if (st != KD_OK) return st;
   *bytes_out = make_layout(T, d, V, K, chunk, dtype).total;
+  return KD_OK;
+}
+
+int kd_topk_kl_fwd_workspace_size(int64_t T, int64_t d, int64_t V, int32_t K,
+                                  int32_t chunk, kd_dtype dtype, size_t *bytes_out) {
+  if (!bytes_out) return KD_ERR_INVALID_ARG;
+  const int st = check_sizes(T, d, V, K, chunk, dtype);
+  if (st != KD_OK) return st;
+  *bytes_out = make_layout(T, d, V, K, chunk, dtype, /*fwd_only=*/true).total;
   return KD_OK;
 }
 
@@ -349,9 +359,11 @@ int kd_topk_kl_fwd(const void *H, const void *W, kd_dtype dtype,
                    size_t workspace_bytes, void *stream) {
   if (!H || !W || !topk_idx || !topk_logit || !loss || misaligned16(H) || misaligned16(W))
     return KD_ERR_INVALID_ARG;
+  // the forward's own (compact) layout: no probabilities, G, gradient
+  // factors, dH partials or transposed hidden states
   return run_loss(MODE_FWD, H, W, dtype, topk_idx, topk_logit, mask, T, d, V, K,
                   tau, chunk, 0u, nullptr, loss, row_loss, lse, nullptr, nullptr,
-                  workspace, workspace_bytes, stream);
+                  workspace, workspace_bytes, stream, /*compact=*/true);
 }
 
 }  // extern "C"
